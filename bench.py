@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the 1-bit Adam compression-phase step on one MI355X.
+
+One step = ob_step over the whole tensor list: all W workers' momentum,
+error feedback and 1-bit compression, the server's average and
+re-compression, and the frozen-variance parameter update.  Inputs are
+synthetic (seeded, generated on the device) and resident in HBM before the
+timed region; a small pool of gradient sets is cycled so successive steps
+see different gradients.
+
+Prints one JSON line on stdout: elements/s of the whole step, the HBM
+roofline of the dominant kernel (timed with HIP events on the launch stream
+inside the timed region), the whole step's algorithmic GB/s, and the oracle
+timed on a bounded sample on the host as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "compressed optimizer-step elements/s and HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def grad_bytes(wl) -> int:
+    return 2 if wl.grad_dtype == "bf16" else 4
+
+
+def step_bytes_per_element(wl) -> float:
+    """Bytes the method itself moves per parameter element per step, each
+    operand touched once: gradients g*W, worker errors read and written 8W,
+    momentum 8, server error 8, variance 4, parameters 8, and the sign
+    messages written and read back W/8 + W/8."""
+    W = wl.workers
+    return 28.0 + (8.0 + grad_bytes(wl)) * W + W / 4.0
+
+
+def kernel_bytes_per_element(wl) -> dict:
+    """Bytes per element each kernel must move, its operands touched once."""
+    W, g = wl.workers, grad_bytes(wl)
+    return {
+        "worker_pass1": 4.0 + (g + 4.0) * W + W / 8.0,        # read m, g, e; write signs
+        "worker_pass2": 4.0 + (g + 4.0) * W + 4.0 * W,        # read m, g, e; write e
+        "server_pass1": W / 8.0 + 4.0,                        # read signs, e_s
+        "server_pass2_update": W / 8.0 + 16.0 + 12.0 + 1 / 8.0,  # read signs, e_s, v, p; write e_s, m, p, signs
+    }
+
+
+def cpu_baseline(wl, state, grads, sample_tensors: int) -> dict:
+    """The oracle, as it stands, on the first `sample_tensors` tensors for one step."""
+    import numpy as np  # noqa: F401
+    import oracle.onebit as ob
+    from synth import host_slice
+    from synth.workloads import padded_layout
+    off, _ = padded_layout(wl.numel)
+    tensors = list(range(min(sample_tensors, wl.num_tensors)))
+    states, gs = [], []
+    for t in tensors:
+        lo, hi = off[t], off[t] + wl.numel[t]
+        states.append(ob.TensorState(host_slice(state["p"], lo, hi), host_slice(state["m"], lo, hi),
+                                     host_slice(state["v"], lo, hi), host_slice(state["err_s"], lo, hi),
+                                     host_slice(state["err_w"], lo, hi)))
+        gs.append(host_slice(grads, lo, hi))
+    n = sum(wl.numel[t] for t in tensors)
+    t0 = time.perf_counter()
+    ob.compression_step_all(states, gs, wl.beta1, wl.lr, wl.eps)
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": n / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {len(tensors)} tensors ({n} elements), 1 step, W={wl.workers}; "
+                      f"{dt:.1f} s on one core of {cpu}",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--grad-sets", type=int, default=4, help="distinct gradient sets cycled")
+    ap.add_argument("--cpu-sample-tensors", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "
+            f"(all W simulated workers share one GPU's HBM)")
+        return 2
+
+    import torch
+    from error_compensated_bit_02_amd import OneBitAdam
+    from synth import WORKLOADS, grads_for_step, init_state
+
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        return 1
+    wl = WORKLOADS[args.workload]
+    n_elem = sum(wl.numel)
+    log(f"bench: {wl.name}: {wl.num_tensors} tensors, {n_elem} elements, W={wl.workers}, "
+        f"grads {wl.grad_dtype}; steps={args.steps} warmup={args.warmup}")
+    ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
+    st = init_state(wl, "cuda")
+    bufs = ctx.alloc("cuda")
+    sets = max(1, min(args.grad_sets, args.steps + args.warmup))
+    grads = [grads_for_step(wl, k, "cuda") for k in range(sets)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(k: int) -> None:
+        ctx.step(grads[k % sets], st["m"], st["v"], st["p"], st["err_w"], st["err_s"],
+                 bufs["packed_w"], bufs["scale_w"], bufs["packed_s"], bufs["scale_s"], wl.lr,
+                 stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    ctx.profile(True)
+    ctx.profile_read(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kernels = ctx.profile_read(reset=True)
+    ctx.profile(False)
+    log(f"bench: timed {args.steps} steps in {dt * 1e3:.2f} ms")
+
+    ms_step = dt * 1e3 / args.steps
+    value = n_elem * args.steps / dt
+    b_alg = step_bytes_per_element(wl)
+    step_gbps = b_alg * n_elem / (ms_step * 1e-3) / 1e9
+
+    per_kernel = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n} for k, (ms, n) in kernels.items()}
+    kb = kernel_bytes_per_element(wl)
+    dom = max((k for k in kb if per_kernel[k]["launches"]), key=lambda k: per_kernel[k]["avg_ms"])
+    dom_ms = per_kernel[dom]["avg_ms"]
+    achieved = kb[dom] * n_elem / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "bytes_per_element": kb[dom], "avg_ms": round(dom_ms, 4)}
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tensors": wl.num_tensors, "elements": n_elem,
+                   "workers": wl.workers, "grad_dtype": wl.grad_dtype,
+                   "grad_sets": sets},
+        "step_hbm_gbps_algorithmic": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "step_bytes_per_element": b_alg,
+        "worker_elements_per_s": value * wl.workers,
+        "roofline": roofline,
+        "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
+                    for k, v in per_kernel.items() if v["launches"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host (cpu baseline)")
+        result["cpu_baseline"] = cpu_baseline(wl, st, grads[0], args.cpu_sample_tensors)
+    ctx.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

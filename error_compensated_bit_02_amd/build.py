@@ -1,0 +1,55 @@
+"""Builds the HIP library libob.so in-tree for gfx950 with hipcc.
+
+Run as ``python -m error_compensated_bit_02_amd.build``.  The flags matter for
+correctness: fp32 products and sums must not be contracted into fused
+multiply-adds, and fp32 division and square root must be correctly rounded.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libob.so")
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3", "-fPIC", "-shared", "-std=c++17",
+    "-ffp-contract=off",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libob.so next to this file; returns its path.  Always recompiles."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,328 @@
+// Host side of the C ABI declared in include/ob.h: argument checks, the
+// padded layout and tile table, scratch ownership, launch sequencing and the
+// optional per-kernel event timing.
+#include "ob.h"
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+struct EventPair {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+}  // namespace
+
+struct ob_ctx {
+  int32_t T = 0;
+  int32_t W = 0;
+  bool bf16 = false;
+  float c1 = 0.0f;
+  float c2 = 0.0f;
+  float eps = 0.0f;
+  std::vector<int64_t> numel;
+  std::vector<int64_t> off;
+  int64_t N = 0;
+  int32_t num_tiles = 0;
+  void *scratch = nullptr;         // one device allocation: tiles | tile_begin | numel | partials
+  ob::Geometry geo{};
+  double2 *partials = nullptr;     // (W+1) x num_tiles
+  bool profiling = false;
+  std::vector<EventPair> pending[ob::K_NUM_KINDS];
+  std::vector<EventPair> pool;
+};
+
+namespace {
+
+const char *const kKindNames[ob::K_NUM_KINDS] = {
+    "worker_pass1", "scale_finalize", "worker_pass2", "server_pass1",
+    "server_pass2", "server_pass2_update", "apply_update"};
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void *p) {
+  if (p == nullptr) return OB_ERR_INVALID;
+  if (!aligned16(p)) return OB_ERR_ALIGN;
+  return OB_OK;
+}
+
+template <typename... P>
+int check_ptrs(const P *...ps) {
+  int st = OB_OK;
+  const void *list[] = {static_cast<const void *>(ps)...};
+  for (const void *p : list) {
+    const int r = check_ptr(p);
+    if (r == OB_ERR_INVALID) return r;
+    if (r != OB_OK) st = r;
+  }
+  return st;
+}
+
+// Brackets one launch with events when profiling is on.
+template <typename F>
+int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
+  EventPair ev;
+  if (c->profiling) {
+    if (!c->pool.empty()) {
+      ev = c->pool.back();
+      c->pool.pop_back();
+    } else if (hipEventCreate(&ev.start) != hipSuccess || hipEventCreate(&ev.stop) != hipSuccess) {
+      return OB_ERR_DEVICE;
+    }
+    if (hipEventRecord(ev.start, s) != hipSuccess) return OB_ERR_DEVICE;
+  }
+  launch();
+  if (hipGetLastError() != hipSuccess) return OB_ERR_DEVICE;
+  if (c->profiling) {
+    if (hipEventRecord(ev.stop, s) != hipSuccess) return OB_ERR_DEVICE;
+    c->pending[kind].push_back(ev);
+  }
+  return OB_OK;
+}
+
+int do_compress(ob_ctx *c, int w0, int w1, const void *grads, const float *m, float *err_w,
+                uint64_t *packed_w, float *scale_w, hipStream_t s) {
+  const ob::Geometry &g = c->geo;
+  int st;
+  st = timed(c, ob::K_WORKER_PASS1, s, [&] {
+    ob::launch_worker_pass1(g, c->bf16, w0, w1, grads, m, err_w, packed_w, c->partials, c->c1,
+                            c->c2, s);
+  });
+  if (st) return st;
+  st = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
+    ob::launch_scale_finalize(g, c->partials, w0, w1 - w0,
+                              scale_w + static_cast<size_t>(w0) * c->T, s);
+  });
+  if (st) return st;
+  return timed(c, ob::K_WORKER_PASS2, s, [&] {
+    ob::launch_worker_pass2(g, c->bf16, w0, w1, grads, m, err_w, scale_w, c->c1, c->c2, s);
+  });
+}
+
+int do_server_first(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, float *err_s,
+                    float *scale_s, hipStream_t s) {
+  const ob::Geometry &g = c->geo;
+  int st = timed(c, ob::K_SERVER_PASS1, s, [&] {
+    ob::launch_server_pass1(g, packed_w, scale_w, err_s, c->partials, s);
+  });
+  if (st) return st;
+  return timed(c, ob::K_SCALE_FINALIZE, s, [&] {
+    ob::launch_scale_finalize(g, c->partials, c->W, 1, scale_s, s);
+  });
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ob_status_string(int status) {
+  switch (status) {
+    case OB_OK: return "ok";
+    case OB_ERR_INVALID: return "invalid argument";
+    case OB_ERR_ALIGN: return "device pointer not aligned to 16 bytes";
+    case OB_ERR_NOMEM: return "out of memory";
+    case OB_ERR_DEVICE: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off) {
+  if (num_tensors < 1 || numel == nullptr || elem_off == nullptr) return OB_ERR_INVALID;
+  int64_t off = 0;
+  for (int32_t t = 0; t < num_tensors; ++t) {
+    if (numel[t] < 1 || numel[t] > (int64_t{1} << 40)) return OB_ERR_INVALID;
+  }
+  for (int32_t t = 0; t < num_tensors; ++t) {
+    elem_off[t] = off;
+    off += (numel[t] + 63) / 64 * 64;
+  }
+  elem_off[num_tensors] = off;
+  return OB_OK;
+}
+
+int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num_workers,
+            int32_t grad_dtype, double beta1, double eps) {
+  if (out == nullptr) return OB_ERR_INVALID;
+  *out = nullptr;
+  if (num_workers < 1 || num_workers > 4096) return OB_ERR_INVALID;
+  if (grad_dtype != OB_GRAD_F32 && grad_dtype != OB_GRAD_BF16) return OB_ERR_INVALID;
+  if (!std::isfinite(beta1) || beta1 < 0.0 || beta1 >= 1.0) return OB_ERR_INVALID;
+  if (!std::isfinite(eps) || eps <= 0.0) return OB_ERR_INVALID;
+  std::vector<int64_t> off(static_cast<size_t>(num_tensors > 0 ? num_tensors : 0) + 1);
+  const int lay = ob_layout(num_tensors, numel, off.data());
+  if (lay != OB_OK) return lay;
+
+  ob_ctx *c = new (std::nothrow) ob_ctx();
+  if (c == nullptr) return OB_ERR_NOMEM;
+  c->T = num_tensors;
+  c->W = num_workers;
+  c->bf16 = grad_dtype == OB_GRAD_BF16;
+  c->c1 = static_cast<float>(beta1);
+  c->c2 = static_cast<float>(1.0 - beta1);
+  c->eps = static_cast<float>(eps);
+  c->numel.assign(numel, numel + num_tensors);
+  c->off = off;
+  c->N = off[num_tensors];
+
+  std::vector<ob::Tile> tiles;
+  std::vector<int32_t> tile_begin(static_cast<size_t>(num_tensors) + 1);
+  for (int32_t t = 0; t < num_tensors; ++t) {
+    tile_begin[t] = static_cast<int32_t>(tiles.size());
+    for (int64_t k = 0; k < numel[t]; k += ob::kTile) {
+      const int64_t len = numel[t] - k < ob::kTile ? numel[t] - k : ob::kTile;
+      tiles.push_back(ob::Tile{off[t] + k, static_cast<int32_t>(len), t});
+    }
+    if (tiles.size() > 0x7fffffffu) {
+      delete c;
+      return OB_ERR_INVALID;
+    }
+  }
+  tile_begin[num_tensors] = static_cast<int32_t>(tiles.size());
+  c->num_tiles = static_cast<int32_t>(tiles.size());
+
+  // one allocation, 256-byte aligned sections
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t b_tiles = up(tiles.size() * sizeof(ob::Tile));
+  const size_t b_begin = up(tile_begin.size() * sizeof(int32_t));
+  const size_t b_numel = up(c->numel.size() * sizeof(int64_t));
+  const size_t b_part = up(static_cast<size_t>(num_workers + 1) * tiles.size() * sizeof(double2));
+  std::vector<unsigned char> host(b_tiles + b_begin + b_numel, 0);
+  std::copy(reinterpret_cast<const unsigned char *>(tiles.data()),
+            reinterpret_cast<const unsigned char *>(tiles.data() + tiles.size()), host.data());
+  std::copy(reinterpret_cast<const unsigned char *>(tile_begin.data()),
+            reinterpret_cast<const unsigned char *>(tile_begin.data() + tile_begin.size()),
+            host.data() + b_tiles);
+  std::copy(reinterpret_cast<const unsigned char *>(c->numel.data()),
+            reinterpret_cast<const unsigned char *>(c->numel.data() + c->numel.size()),
+            host.data() + b_tiles + b_begin);
+  if (hipMalloc(&c->scratch, host.size() + b_part) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return OB_ERR_NOMEM;
+  }
+  if (hipMemcpy(c->scratch, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(c->scratch);
+    delete c;
+    return OB_ERR_DEVICE;
+  }
+  unsigned char *base = static_cast<unsigned char *>(c->scratch);
+  c->geo.tiles = reinterpret_cast<const ob::Tile *>(base);
+  c->geo.tile_begin = reinterpret_cast<const int32_t *>(base + b_tiles);
+  c->geo.numel = reinterpret_cast<const int64_t *>(base + b_tiles + b_begin);
+  c->partials = reinterpret_cast<double2 *>(base + b_tiles + b_begin + b_numel);
+  c->geo.num_tiles = c->num_tiles;
+  c->geo.T = c->T;
+  c->geo.W = c->W;
+  c->geo.N = c->N;
+  c->geo.Nw = c->N / 64;
+  *out = c;
+  return OB_OK;
+}
+
+void ob_destroy(ob_ctx *c) {
+  if (c == nullptr) return;
+  for (auto &v : c->pending)
+    for (auto &e : v) c->pool.push_back(e);
+  for (auto &e : c->pool) {
+    if (e.start) (void)hipEventDestroy(e.start);
+    if (e.stop) (void)hipEventDestroy(e.stop);
+  }
+  if (c->scratch) (void)hipFree(c->scratch);
+  delete c;
+}
+
+int ob_compress_worker(ob_ctx *c, int32_t w_begin, int32_t w_end, const void *grads,
+                       const float *m, float *err_w, uint64_t *packed_w, float *scale_w,
+                       void *stream) {
+  if (c == nullptr) return OB_ERR_INVALID;
+  if (w_begin < 0 || w_end > c->W || w_begin >= w_end) return OB_ERR_INVALID;
+  const int st = check_ptrs(grads, m, err_w, packed_w, scale_w);
+  if (st) return st;
+  return do_compress(c, w_begin, w_end, grads, m, err_w, packed_w, scale_w,
+                     static_cast<hipStream_t>(stream));
+}
+
+int ob_server_reduce(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, float *err_s,
+                     uint64_t *packed_s, float *scale_s, void *stream) {
+  if (c == nullptr) return OB_ERR_INVALID;
+  const int st = check_ptrs(packed_w, scale_w, err_s, packed_s, scale_s);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int r = do_server_first(c, packed_w, scale_w, err_s, scale_s, s);
+  if (r) return r;
+  return timed(c, ob::K_SERVER_PASS2, s, [&] {
+    ob::launch_server_pass2(c->geo, false, packed_w, scale_w, err_s, scale_s, packed_s, nullptr,
+                            nullptr, nullptr, 0.0f, 0.0f, s);
+  });
+}
+
+int ob_apply_update(ob_ctx *c, const uint64_t *packed_s, const float *scale_s, const float *v,
+                    float *m, float *params, double lr, void *stream) {
+  if (c == nullptr || !std::isfinite(lr)) return OB_ERR_INVALID;
+  const int st = check_ptrs(packed_s, scale_s, v, m, params);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, ob::K_APPLY_UPDATE, s, [&] {
+    ob::launch_apply_update(c->geo, packed_s, scale_s, v, m, params, static_cast<float>(lr), c->eps,
+                            s);
+  });
+}
+
+int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *params, float *err_w,
+            float *err_s, uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s,
+            double lr, void *stream) {
+  if (c == nullptr || !std::isfinite(lr)) return OB_ERR_INVALID;
+  const int st = check_ptrs(grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s, scale_s);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r = do_compress(c, 0, c->W, grads, m, err_w, packed_w, scale_w, s);
+  if (r) return r;
+  r = do_server_first(c, packed_w, scale_w, err_s, scale_s, s);
+  if (r) return r;
+  return timed(c, ob::K_SERVER_PASS2_UPDATE, s, [&] {
+    ob::launch_server_pass2(c->geo, true, packed_w, scale_w, err_s, scale_s, packed_s, v, m,
+                            params, static_cast<float>(lr), c->eps, s);
+  });
+}
+
+int ob_profile_enable(ob_ctx *c, int32_t enable) {
+  if (c == nullptr) return OB_ERR_INVALID;
+  c->profiling = enable != 0;
+  return OB_OK;
+}
+
+int32_t ob_profile_kinds(void) { return ob::K_NUM_KINDS; }
+
+const char *ob_profile_kind_name(int32_t kind) {
+  if (kind < 0 || kind >= ob::K_NUM_KINDS) return nullptr;
+  return kKindNames[kind];
+}
+
+int ob_profile_read(ob_ctx *c, double *total_ms, int64_t *launches, int32_t reset) {
+  if (c == nullptr || total_ms == nullptr || launches == nullptr) return OB_ERR_INVALID;
+  for (int k = 0; k < ob::K_NUM_KINDS; ++k) {
+    double sum = 0.0;
+    for (auto &e : c->pending[k]) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(e.stop) != hipSuccess) return OB_ERR_DEVICE;
+      if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess) return OB_ERR_DEVICE;
+      sum += ms;
+    }
+    total_ms[k] = sum;
+    launches[k] = static_cast<int64_t>(c->pending[k].size());
+    if (reset) {
+      for (auto &e : c->pending[k]) c->pool.push_back(e);
+      c->pending[k].clear();
+    }
+  }
+  return OB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+/*
+ * ob.h — C ABI of the 1-bit Adam compression-phase step on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method: the nubint.ai review of "1-bit Adam: Communication Efficient
+ * Large-Scale Training with Adam's Convergence Speed" (Tang, Gan et al.).
+ * After a full-precision Adam warmup, Adam's variance is frozen and used as a
+ * fixed preconditioner (Abstract; Proposed method, bullet 2), and training
+ * continues as momentum SGD whose momentum is exchanged with 1-bit
+ * error-compensated compression (One-line summary; Proposed method, bullets
+ * 1 and 3).  The review's system exchanges the compressed messages with
+ * custom collectives (Proposed method, bullet 4).  Here all W workers'
+ * buffers live in one GPU's HBM and the exchange is a local reduction over
+ * the W packed messages.
+ *
+ * Arithmetic (the pages give no formulas; these are the readings taken):
+ *   c1 = fp32(beta1), c2 = fp32(1 - beta1) (complement in double, rounded once)
+ *   worker w, element i of tensor t (every fp32 operation rounded once, no FMA):
+ *     x        = (c1*m[i] + c2*g_w[i]) + e_w[i]
+ *     bit      = x >= 0            (+0 and -0 give 1, NaN gives 0)
+ *     s_w,t    = fp32( sqrt( fl64(sum over tensor t of x^2) / n_t ) )
+ *     e_w[i]   = bit ? x - s_w,t : x + s_w,t
+ *   server:
+ *     y        = (sum over w = 0..W-1, ascending, from +0, of (bit_w ? s_w,t : -s_w,t)) / W
+ *     z        = y + e_s[i];  bit_s = z >= 0;  s_s,t as above over z
+ *     e_s[i]   = bit_s ? z - s_s,t : z + s_s,t
+ *   update:
+ *     m[i]     = bit_s ? s_s,t : -s_s,t
+ *     p[i]     = p[i] - lr * (m[i] / (sqrt(v[i]) + eps))   (correctly rounded sqrt and /)
+ *   A tensor holding a non-finite x (or z) gets a NaN scale.
+ *
+ * Layout.  T tensors with n_t >= 1 elements.  Every flat buffer uses the same
+ * padded layout: tensor t occupies elements [off[t], off[t] + n_t) with
+ * off[0] = 0 and off[t+1] = off[t] + 64*ceil(n_t/64); N = off[T].  Elements in
+ * [off[t] + n_t, off[t+1]) are padding: never read, never written.
+ * Per-worker buffers are [W][N] with row stride N.  A packed sign message is
+ * uint64 words, Nw = N/64 per worker: word j, bit k holds element 64*j + k;
+ * each tensor starts on a word; bits past a tensor's end are written as 0.
+ * Scales are fp32: scale_w is [W][T] (row stride T), scale_s is [T].
+ *
+ * Ownership.  The caller owns every buffer passed in: device memory (HBM)
+ * pointers, each aligned to 16 bytes.  The library owns only the context and
+ * its scratch (a tile table and per-tile partial sums, allocated in ob_init).
+ *
+ * Streams.  Every device call enqueues its kernels on the given stream (a
+ * hipStream_t; NULL means the null stream) and returns without waiting.
+ * Results are visible to later work on that stream.  Concurrent calls on one
+ * context from several host threads, or on several streams at once, race on
+ * the context's scratch and are not allowed.
+ *
+ * Errors.  Calls return OB_OK or an ob_status code.  Argument errors are
+ * detected before anything is enqueued.  A failed launch returns
+ * OB_ERR_DEVICE; faults inside a kernel surface at the caller's next
+ * synchronization with the stream.
+ */
+#ifndef OB_H
+#define OB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ob_ctx ob_ctx;
+
+typedef enum {
+  OB_OK = 0,
+  OB_ERR_INVALID = 1,   /* null pointer, bad count, bad range, non-finite hyper-parameter */
+  OB_ERR_ALIGN = 2,     /* a device pointer not aligned to 16 bytes */
+  OB_ERR_NOMEM = 3,     /* device or host allocation failed */
+  OB_ERR_DEVICE = 4     /* a HIP runtime call or kernel launch failed */
+} ob_status;
+
+typedef enum {
+  OB_GRAD_F32 = 0,      /* gradients are IEEE binary32 */
+  OB_GRAD_BF16 = 1      /* gradients are bfloat16 (widened exactly to fp32) */
+} ob_grad_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *ob_status_string(int status);
+
+/* Host only (no device access).  Fills elem_off[0..T] with the padded layout
+ * described above for numel[0..T-1].  Returns OB_ERR_INVALID if T < 1, a
+ * pointer is NULL or some numel[t] < 1. */
+int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off);
+
+/* Creates a context for T tensors of numel[] elements (host array, copied),
+ * W >= 1 simulated workers, gradients of grad_dtype, and the fixed
+ * hyper-parameters beta1 (momentum, in [0, 1)) and eps (> 0).  Allocates the
+ * context's device scratch on the current HIP device and uploads its tile
+ * table with one synchronous copy: the only blocking call of this library. */
+int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num_workers,
+            int32_t grad_dtype, double beta1, double eps);
+
+/* Frees the context and its scratch (waits for the device as hipFree does).
+ * NULL is ignored. */
+void ob_destroy(ob_ctx *ctx);
+
+/* Workers [w_begin, w_end) ⊆ [0, W): momentum, error feedback, 1-bit
+ * compression and the new worker error.
+ *   grads    [W][N] grad_dtype, read (rows w_begin..w_end-1)
+ *   m        [N]    fp32, read (the shared momentum)
+ *   err_w    [W][N] fp32, read and overwritten with the new errors
+ *   packed_w [W][Nw] uint64, written (the messages)
+ *   scale_w  [W][T] fp32, written */
+int ob_compress_worker(ob_ctx *ctx, int32_t w_begin, int32_t w_end, const void *grads,
+                       const float *m, float *err_w, uint64_t *packed_w, float *scale_w,
+                       void *stream);
+
+/* Server: decompress and average all W messages, add the server error,
+ * re-compress, store the new server error.
+ *   packed_w [W][Nw], scale_w [W][T] read; err_s [N] read and overwritten;
+ *   packed_s [Nw] and scale_s [T] written (the server message). */
+int ob_server_reduce(ob_ctx *ctx, const uint64_t *packed_w, const float *scale_w,
+                     float *err_s, uint64_t *packed_s, float *scale_s, void *stream);
+
+/* Update from the server message with the frozen variance:
+ *   packed_s [Nw], scale_s [T], v [N] read; m [N] written; params [N] read and
+ *   overwritten.  lr must be finite. */
+int ob_apply_update(ob_ctx *ctx, const uint64_t *packed_s, const float *scale_s,
+                    const float *v, float *m, float *params, double lr, void *stream);
+
+/* One whole compression-phase step: ob_compress_worker over all W workers,
+ * ob_server_reduce and ob_apply_update, with the server's second pass and the
+ * update fused into one kernel.  Same buffers and results as the three calls
+ * in sequence. */
+int ob_step(ob_ctx *ctx, const void *grads, float *m, const float *v, float *params,
+            float *err_w, float *err_s, uint64_t *packed_w, float *scale_w,
+            uint64_t *packed_s, float *scale_s, double lr, void *stream);
+
+/* Kernel timing for measurement.  With profiling on, every kernel the context
+ * launches is bracketed by HIP events on its stream.  ob_profile_read waits for
+ * the recorded events, writes per kernel kind the summed milliseconds and the
+ * launch count (arrays of ob_profile_kinds() entries), and with reset != 0
+ * forgets them.  ob_profile_kind_name names kind k (NULL when out of range). */
+int ob_profile_enable(ob_ctx *ctx, int32_t enable);
+int32_t ob_profile_kinds(void);
+const char *ob_profile_kind_name(int32_t kind);
+int ob_profile_read(ob_ctx *ctx, double *total_ms, int64_t *launches, int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OB_H */
