@@ -98,7 +98,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct gradient sets cycled")
-    ap.add_argument("--cpu-sample-tensors", type=int, default=16)
+    ap.add_argument("--cpu-sample-tensors", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
