@@ -54,6 +54,10 @@ def kernel_bytes_per_element(wl) -> dict:
         "worker_pass2": 4.0 + (g + 4.0) * W + 4.0 * W,        # read m, g, e; write e
         "server_pass1": W / 8.0 + 4.0,                        # read signs, e_s
         "server_pass2_update": W / 8.0 + 16.0 + 12.0 + 1 / 8.0,  # read signs, e_s, v, p; write e_s, m, p, signs
+        # residual form: read g, x_prev and the previous server signs (the momentum); write x, signs
+        "worker_residual": (g + 8.0) * W + W / 8.0 + 1 / 8.0,
+        "server_residual": W / 8.0 + 8.0 + 1 / 8.0,           # read signs, z_prev; write z, server signs
+        "update_residual": 1 / 8.0 + 12.0,                    # read server signs, v, p; write p
     }
 
 
@@ -91,15 +95,79 @@ def cpu_baseline(wl, state, grads, sample_tensors: int) -> dict:
             "seconds": dt}
 
 
+def time_form(form, wl, ctx, grads, steps, warmup, stream):
+    """Warmup, then `steps` timed steps of one state form from a fresh state.
+    Returns (seconds, {kernel: (total ms, launches)}) over the timed region."""
+    import torch
+    from synth import init_state
+    st = init_state(wl, "cuda")
+    bufs = ctx.alloc("cuda")
+    sets = len(grads)
+
+    def step(k: int) -> None:
+        if form == "residual":
+            ctx.step_residual(k == 0, grads[k % sets], st["m"], st["v"], st["p"], st["err_w"],
+                              st["err_s"], bufs["packed_w"], bufs["scale_w"], bufs["packed_s"],
+                              bufs["scale_s"], wl.lr, stream=stream)
+        else:
+            ctx.step(grads[k % sets], st["m"], st["v"], st["p"], st["err_w"], st["err_s"],
+                     bufs["packed_w"], bufs["scale_w"], bufs["packed_s"], bufs["scale_s"], wl.lr,
+                     stream=stream)
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    ctx.profile_read(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(warmup + k)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kernels = ctx.profile_read(reset=True)
+    ctx.profile(False)
+    return dt, kernels, st
+
+
+def summarize(wl, n_elem, steps, dt, kernels):
+    ms_step = dt * 1e3 / steps
+    b_alg = step_bytes_per_element(wl)
+    step_gbps = b_alg * n_elem / (ms_step * 1e-3) / 1e9
+    per_kernel = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n} for k, (ms, n) in kernels.items()}
+    kb = kernel_bytes_per_element(wl)
+    dom = max((k for k in kb if per_kernel[k]["launches"]), key=lambda k: per_kernel[k]["avg_ms"])
+    dom_ms = per_kernel[dom]["avg_ms"]
+    achieved = kb[dom] * n_elem / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "bytes_per_element": kb[dom], "avg_ms": round(dom_ms, 4)}
+    return {
+        "ms_per_step": ms_step,
+        "value": n_elem * steps / dt,
+        "step_hbm_gbps_algorithmic": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
+                    for k, v in per_kernel.items() if v["launches"]},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--form", choices=("both", "residual", "strict"), default="both",
+                    help="state form between steps; both forms give bit-identical trajectories. "
+                         "'both' times the residual form (the headline) and the strict form")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct gradient sets cycled")
     ap.add_argument("--cpu-sample-tensors", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 launches) for calibrating "
+                         "HBM byte counters, then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -109,79 +177,63 @@ def main() -> int:
 
     import torch
     from error_compensated_bit_02_amd import OneBitAdam
-    from synth import WORKLOADS, grads_for_step, init_state
+    from synth import WORKLOADS, grads_for_step
 
     if not torch.cuda.is_available():
         log("bench.py: no GPU visible")
         return 1
+    if args.copy_calibration:
+        n = args.copy_calibration << 18            # fp32 elements in MIB MiB
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {args.copy_calibration} MiB three times "
+            f"(each launch reads and writes {args.copy_calibration} MiB)")
+        return 0
     wl = WORKLOADS[args.workload]
     n_elem = sum(wl.numel)
     log(f"bench: {wl.name}: {wl.num_tensors} tensors, {n_elem} elements, W={wl.workers}, "
         f"grads {wl.grad_dtype}; steps={args.steps} warmup={args.warmup}")
     ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
-    st = init_state(wl, "cuda")
-    bufs = ctx.alloc("cuda")
     sets = max(1, min(args.grad_sets, args.steps + args.warmup))
     grads = [grads_for_step(wl, k, "cuda") for k in range(sets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(k: int) -> None:
-        ctx.step(grads[k % sets], st["m"], st["v"], st["p"], st["err_w"], st["err_s"],
-                 bufs["packed_w"], bufs["scale_w"], bufs["packed_s"], bufs["scale_s"], wl.lr,
-                 stream=stream)
+    forms = ["residual", "strict"] if args.form == "both" else [args.form]
+    results, last_state = {}, None
+    for form in forms:
+        last_state = None
+        torch.cuda.empty_cache()
+        dt, kernels, last_state = time_form(form, wl, ctx, grads, args.steps, args.warmup, stream)
+        results[form] = summarize(wl, n_elem, args.steps, dt, kernels)
+        log(f"bench: {form}: {results[form]['ms_per_step']:.3f} ms/step, "
+            f"{100 * results[form]['step_frac_of_peak']:.1f}% of peak")
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    log("bench: warmup done")
-
-    ctx.profile(True)
-    ctx.profile_read(reset=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    kernels = ctx.profile_read(reset=True)
-    ctx.profile(False)
-    log(f"bench: timed {args.steps} steps in {dt * 1e3:.2f} ms")
-
-    ms_step = dt * 1e3 / args.steps
-    value = n_elem * args.steps / dt
-    b_alg = step_bytes_per_element(wl)
-    step_gbps = b_alg * n_elem / (ms_step * 1e-3) / 1e9
-
-    per_kernel = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n} for k, (ms, n) in kernels.items()}
-    kb = kernel_bytes_per_element(wl)
-    dom = max((k for k in kb if per_kernel[k]["launches"]), key=lambda k: per_kernel[k]["avg_ms"])
-    dom_ms = per_kernel[dom]["avg_ms"]
-    achieved = kb[dom] * n_elem / (dom_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "bytes_per_element": kb[dom], "avg_ms": round(dom_ms, 4)}
-
+    head = results[forms[0]]
     result = {
-        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "metric": METRIC, "value": head["value"], "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "tensors": wl.num_tensors, "elements": n_elem,
                    "workers": wl.workers, "grad_dtype": wl.grad_dtype,
-                   "grad_sets": sets},
-        "step_hbm_gbps_algorithmic": round(step_gbps, 1),
-        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "step_bytes_per_element": b_alg,
-        "worker_elements_per_s": value * wl.workers,
-        "roofline": roofline,
-        "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
-                    for k, v in per_kernel.items() if v["launches"]},
-        "cpu_baseline": None,
+                   "grad_sets": sets, "state_form": forms[0]},
+        "step_hbm_gbps_algorithmic": head["step_hbm_gbps_algorithmic"],
+        "step_frac_of_peak": head["step_frac_of_peak"],
+        "step_bytes_per_element": step_bytes_per_element(wl),
+        "worker_elements_per_s": head["value"] * wl.workers,
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
     }
+    if "strict" in results and forms[0] != "strict":
+        result["strict_form"] = results["strict"]
+    result["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (cpu baseline)")
-        result["cpu_baseline"] = cpu_baseline(wl, st, grads[0], args.cpu_sample_tensors)
+        result["cpu_baseline"] = cpu_baseline(wl, last_state, grads[0], args.cpu_sample_tensors)
     ctx.close()
     print(json.dumps(result), flush=True)
     return 0

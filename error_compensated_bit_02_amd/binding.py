@@ -33,6 +33,8 @@ SIGNATURES = {
     "ob_server_reduce": (ctypes.c_int, [_c_void_p] * 7),
     "ob_apply_update": (ctypes.c_int, [_c_void_p] * 6 + [_f64, _c_void_p]),
     "ob_step": (ctypes.c_int, [_c_void_p] * 11 + [_f64, _c_void_p]),
+    "ob_step_residual": (ctypes.c_int, [_c_void_p, _i32] + [_c_void_p] * 10 + [_f64, _c_void_p]),
+    "ob_materialize": (ctypes.c_int, [_c_void_p] * 9),
     "ob_profile_enable": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_profile_kinds": (_i32, []),
     "ob_profile_kind_name": (ctypes.c_char_p, [_i32]),
@@ -191,6 +193,31 @@ class OneBitAdam:
             _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
             _ptr(scale_s, f32, self.T, "scale_s"), float(lr), _stream(stream))
         _check(st, "ob_step")
+
+    def step_residual(self, first, grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s,
+                      scale_s, lr, stream=None) -> None:
+        """One step with err_w / err_s in residual form (see include/ob.h)."""
+        f32 = (torch.float32,)
+        m_ptr = _ptr(m, f32, self.N, "m") if first else (None if m is None else _ptr(m, f32, self.N, "m"))
+        st = self.lib.ob_step_residual(
+            self._ctx, 1 if first else 0, self._grad_ptr(grads), m_ptr, _ptr(v, f32, self.N, "v"),
+            _ptr(params, f32, self.N, "params"), _ptr(err_w, f32, self.W * self.N, "err_w"),
+            _ptr(err_s, f32, self.N, "err_s"),
+            _ptr(packed_w, (torch.int64,), self.W * self.Nw, "packed_w"),
+            _ptr(scale_w, f32, self.W * self.T, "scale_w"),
+            _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
+            _ptr(scale_s, f32, self.T, "scale_s"), float(lr), _stream(stream))
+        _check(st, "ob_step_residual")
+
+    def materialize(self, x_w, scale_w, z, scale_s, err_w, err_s, m, stream=None) -> None:
+        """Strict-form errors and momentum from a residual-form state (may be in place)."""
+        f32 = (torch.float32,)
+        st = self.lib.ob_materialize(
+            self._ctx, _ptr(x_w, f32, self.W * self.N, "x_w"), _ptr(scale_w, f32, self.W * self.T, "scale_w"),
+            _ptr(z, f32, self.N, "z"), _ptr(scale_s, f32, self.T, "scale_s"),
+            _ptr(err_w, f32, self.W * self.N, "err_w"), _ptr(err_s, f32, self.N, "err_s"),
+            _ptr(m, f32, self.N, "m"), _stream(stream))
+        _check(st, "ob_materialize")
 
     # -- kernel timing -------------------------------------------------------
     def profile(self, enable: bool) -> None:

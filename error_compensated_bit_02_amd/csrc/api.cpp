@@ -43,7 +43,8 @@ namespace {
 
 const char *const kKindNames[ob::K_NUM_KINDS] = {
     "worker_pass1", "scale_finalize", "worker_pass2", "server_pass1",
-    "server_pass2", "server_pass2_update", "apply_update"};
+    "server_pass2", "server_pass2_update", "apply_update", "worker_residual",
+    "server_residual", "update_residual", "materialize"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -87,13 +88,44 @@ int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
   return OB_OK;
 }
 
+ob::WorkerArgs worker_args(ob_ctx *c, int w0, int w1, const void *grads, const float *m,
+                          float *err_w, uint64_t *packed_w, const float *scale_w,
+                          const uint64_t *packed_s, const float *scale_s) {
+  ob::WorkerArgs a{};
+  a.grads = grads;
+  a.m = m;
+  a.err_w = err_w;
+  a.packed_w = packed_w;
+  a.scale_w = scale_w;
+  a.packed_s = packed_s;
+  a.scale_s = scale_s;
+  a.partials = c->partials;
+  a.w0 = w0;
+  a.w1 = w1;
+  a.c1 = c->c1;
+  a.c2 = c->c2;
+  return a;
+}
+
+ob::ServerArgs server_args(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, float *err_s,
+                          const float *scale_s, uint64_t *packed_s) {
+  ob::ServerArgs a{};
+  a.packed_w = packed_w;
+  a.scale_w = scale_w;
+  a.err_s = err_s;
+  a.partials = c->partials;
+  a.scale_s = scale_s;
+  a.packed_s = packed_s;
+  a.eps = c->eps;
+  return a;
+}
+
 int do_compress(ob_ctx *c, int w0, int w1, const void *grads, const float *m, float *err_w,
                 uint64_t *packed_w, float *scale_w, hipStream_t s) {
   const ob::Geometry &g = c->geo;
-  int st;
-  st = timed(c, ob::K_WORKER_PASS1, s, [&] {
-    ob::launch_worker_pass1(g, c->bf16, w0, w1, grads, m, err_w, packed_w, c->partials, c->c1,
-                            c->c2, s);
+  const ob::WorkerArgs a = worker_args(c, w0, w1, grads, m, err_w, packed_w, scale_w, nullptr, nullptr);
+  int st = timed(c, ob::K_WORKER_PASS1, s, [&] {
+    ob::launch_worker(ob::WorkerPass::kStrictSigns, g, c->bf16, a, s);
   });
   if (st) return st;
   st = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
@@ -102,15 +134,16 @@ int do_compress(ob_ctx *c, int w0, int w1, const void *grads, const float *m, fl
   });
   if (st) return st;
   return timed(c, ob::K_WORKER_PASS2, s, [&] {
-    ob::launch_worker_pass2(g, c->bf16, w0, w1, grads, m, err_w, scale_w, c->c1, c->c2, s);
+    ob::launch_worker(ob::WorkerPass::kStrictErrors, g, c->bf16, a, s);
   });
 }
 
 int do_server_first(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, float *err_s,
                     float *scale_s, hipStream_t s) {
   const ob::Geometry &g = c->geo;
+  const ob::ServerArgs a = server_args(c, packed_w, scale_w, err_s, nullptr, nullptr);
   int st = timed(c, ob::K_SERVER_PASS1, s, [&] {
-    ob::launch_server_pass1(g, packed_w, scale_w, err_s, c->partials, s);
+    ob::launch_server(ob::ServerPass::kStrictSums, g, a, s);
   });
   if (st) return st;
   return timed(c, ob::K_SCALE_FINALIZE, s, [&] {
@@ -192,7 +225,8 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   const size_t b_tiles = up(tiles.size() * sizeof(ob::Tile));
   const size_t b_begin = up(tile_begin.size() * sizeof(int32_t));
   const size_t b_numel = up(c->numel.size() * sizeof(int64_t));
-  const size_t b_part = up(static_cast<size_t>(num_workers + 1) * tiles.size() * sizeof(double2));
+  const size_t b_part =
+      up(ob::partials_count(num_workers, static_cast<int>(tiles.size())) * sizeof(double2));
   std::vector<unsigned char> host(b_tiles + b_begin + b_numel, 0);
   std::copy(reinterpret_cast<const unsigned char *>(tiles.data()),
             reinterpret_cast<const unsigned char *>(tiles.data() + tiles.size()), host.data());
@@ -257,9 +291,9 @@ int ob_server_reduce(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int r = do_server_first(c, packed_w, scale_w, err_s, scale_s, s);
   if (r) return r;
+  const ob::ServerArgs a = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
   return timed(c, ob::K_SERVER_PASS2, s, [&] {
-    ob::launch_server_pass2(c->geo, false, packed_w, scale_w, err_s, scale_s, packed_s, nullptr,
-                            nullptr, nullptr, 0.0f, 0.0f, s);
+    ob::launch_server(ob::ServerPass::kStrictErrors, c->geo, a, s);
   });
 }
 
@@ -269,10 +303,8 @@ int ob_apply_update(ob_ctx *c, const uint64_t *packed_s, const float *scale_s, c
   const int st = check_ptrs(packed_s, scale_s, v, m, params);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return timed(c, ob::K_APPLY_UPDATE, s, [&] {
-    ob::launch_apply_update(c->geo, packed_s, scale_s, v, m, params, static_cast<float>(lr), c->eps,
-                            s);
-  });
+  const ob::UpdateArgs a{packed_s, scale_s, v, m, params, static_cast<float>(lr), c->eps};
+  return timed(c, ob::K_APPLY_UPDATE, s, [&] { ob::launch_update(true, c->geo, a, s); });
 }
 
 int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *params, float *err_w,
@@ -286,10 +318,58 @@ int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *param
   if (r) return r;
   r = do_server_first(c, packed_w, scale_w, err_s, scale_s, s);
   if (r) return r;
+  ob::ServerArgs a = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
+  a.v = v;
+  a.m = m;
+  a.params = params;
+  a.lr = static_cast<float>(lr);
   return timed(c, ob::K_SERVER_PASS2_UPDATE, s, [&] {
-    ob::launch_server_pass2(c->geo, true, packed_w, scale_w, err_s, scale_s, packed_s, v, m,
-                            params, static_cast<float>(lr), c->eps, s);
+    ob::launch_server(ob::ServerPass::kStrictErrorsUpdate, c->geo, a, s);
   });
+}
+
+int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m, const float *v,
+                     float *params, float *err_w, float *err_s, uint64_t *packed_w, float *scale_w,
+                     uint64_t *packed_s, float *scale_s, double lr, void *stream) {
+  if (c == nullptr || !std::isfinite(lr)) return OB_ERR_INVALID;
+  int st = check_ptrs(grads, v, params, err_w, err_s, packed_w, scale_w, packed_s, scale_s);
+  if (st) return st;
+  if (first && (st = check_ptr(m)) != OB_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ob::Geometry &g = c->geo;
+  // worker: x = (c1*m + c2*g) + e, with e and m formed from the previous step's residual form
+  const ob::WorkerArgs wa = worker_args(c, 0, c->W, grads, first ? m : nullptr, err_w, packed_w,
+                                        scale_w, packed_s, scale_s);
+  int r = timed(c, ob::K_WORKER_RESIDUAL, s, [&] {
+    ob::launch_worker(first ? ob::WorkerPass::kResidualFirst : ob::WorkerPass::kResidual, g,
+                      c->bf16, wa, s);
+  });
+  if (r) return r;
+  r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
+    ob::launch_scale_finalize(g, c->partials, 0, c->W, scale_w, s);
+  });
+  if (r) return r;
+  const ob::ServerArgs sa = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
+  r = timed(c, ob::K_SERVER_RESIDUAL, s, [&] {
+    ob::launch_server(first ? ob::ServerPass::kResidualFirst : ob::ServerPass::kResidual, g, sa, s);
+  });
+  if (r) return r;
+  r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
+    ob::launch_scale_finalize(g, c->partials, c->W, 1, scale_s, s);
+  });
+  if (r) return r;
+  const ob::UpdateArgs ua{packed_s, scale_s, v, nullptr, params, static_cast<float>(lr), c->eps};
+  return timed(c, ob::K_UPDATE_RESIDUAL, s, [&] { ob::launch_update(false, g, ua, s); });
+}
+
+int ob_materialize(ob_ctx *c, const float *x_w, const float *scale_w, const float *z,
+                   const float *scale_s, float *err_w, float *err_s, float *m, void *stream) {
+  if (c == nullptr) return OB_ERR_INVALID;
+  const int st = check_ptrs(x_w, scale_w, z, scale_s, err_w, err_s, m);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ob::MaterializeArgs a{x_w, scale_w, z, scale_s, err_w, err_s, m};
+  return timed(c, ob::K_MATERIALIZE, s, [&] { ob::launch_materialize(c->geo, a, s); });
 }
 
 int ob_profile_enable(ob_ctx *c, int32_t enable) {

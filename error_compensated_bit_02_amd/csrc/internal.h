@@ -13,9 +13,14 @@ namespace ob {
 // l of a wavefront owns element 64*c + l of its range for c < kPerLane, so a
 // wavefront-wide ballot over one c yields one packed sign word in natural
 // bit order.
+// Elements per tile (a multiple of 256); 8192 measured best on gfx950 for
+// the worker passes (4096 and 16384 were slower or spilled).
+#ifndef OB_TILE
+#define OB_TILE 8192
+#endif
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
-constexpr int kTile = 8192;
+constexpr int kTile = OB_TILE;
 constexpr int kSub = kTile / kWaves;
 constexpr int kPerLane = kSub / 64;
 
@@ -37,6 +42,12 @@ struct Geometry {
   int64_t Nw;                 // N / 64 sign words per packed row
 };
 
+// Partial sums of squares: (W+1) rows (workers, then the server) of
+// num_tiles compensated fp64 pairs (hi, lo), one per tile.
+inline size_t partials_count(int W, int num_tiles) {
+  return static_cast<size_t>(W + 1) * static_cast<size_t>(num_tiles);
+}
+
 enum Kind {
   K_WORKER_PASS1 = 0,
   K_SCALE_FINALIZE,
@@ -45,28 +56,66 @@ enum Kind {
   K_SERVER_PASS2,
   K_SERVER_PASS2_UPDATE,
   K_APPLY_UPDATE,
+  K_WORKER_RESIDUAL,
+  K_SERVER_RESIDUAL,
+  K_UPDATE_RESIDUAL,
+  K_MATERIALIZE,
   K_NUM_KINDS
 };
 
-// Kernel launchers (kernels.hip).  partials holds (W+1) rows of num_tiles
-// compensated fp64 sums (hi, lo): rows 0..W-1 for workers, row W for the server.
-void launch_worker_pass1(const Geometry &g, bool bf16, int w0, int w1, const void *grads,
-                         const float *m, const float *err_w, uint64_t *packed_w,
-                         double2 *partials, float c1, float c2, hipStream_t s);
+enum class WorkerPass { kStrictSigns, kStrictErrors, kResidualFirst, kResidual };
+enum class ServerPass { kStrictSums, kStrictErrors, kStrictErrorsUpdate, kResidualFirst, kResidual };
+
+struct WorkerArgs {
+  const void *grads;         // [W][N] fp32 or bf16
+  const float *m;            // [N] momentum (strict and first residual step)
+  float *err_w;              // [W][N] errors (strict) or compressed values (residual)
+  uint64_t *packed_w;        // [W][Nw]
+  const float *scale_w;      // [W][T]: this step's (strict errors) or the previous step's (residual)
+  const uint64_t *packed_s;  // [Nw] previous server message (residual)
+  const float *scale_s;      // [T]  previous server scales (residual)
+  double2 *partials;
+  int w0, w1;
+  float c1, c2;
+};
+
+struct ServerArgs {
+  const uint64_t *packed_w;  // [W][Nw]
+  const float *scale_w;      // [W][T] this step's worker scales
+  float *err_s;              // [N] error (strict) or compressed value (residual)
+  double2 *partials;
+  const float *scale_s;      // [T] this step's (strict) or the previous step's (residual)
+  uint64_t *packed_s;        // [Nw] written
+  const float *v;            // fused strict update only
+  float *m;
+  float *params;
+  float lr, eps;
+};
+
+struct UpdateArgs {
+  const uint64_t *packed_s;
+  const float *scale_s;
+  const float *v;
+  float *m;                  // written when the momentum is stored
+  float *params;
+  float lr, eps;
+};
+
+struct MaterializeArgs {     // inputs and outputs may alias
+  const float *x_w;
+  const float *scale_w;
+  const float *z;
+  const float *scale_s;
+  float *e_w;
+  float *e_s;
+  float *m;
+};
+
+void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s);
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0, int nrows,
                            float *out, hipStream_t s);
-void launch_worker_pass2(const Geometry &g, bool bf16, int w0, int w1, const void *grads,
-                         const float *m, float *err_w, const float *scale_w, float c1, float c2,
-                         hipStream_t s);
-void launch_server_pass1(const Geometry &g, const uint64_t *packed_w, const float *scale_w,
-                         const float *err_s, double2 *partials, hipStream_t s);
-// update == false: writes err_s and packed_s only; update == true: also m and params.
-void launch_server_pass2(const Geometry &g, bool update, const uint64_t *packed_w,
-                         const float *scale_w, float *err_s, const float *scale_s,
-                         uint64_t *packed_s, const float *v, float *m, float *params, float lr,
-                         float eps, hipStream_t s);
-void launch_apply_update(const Geometry &g, const uint64_t *packed_s, const float *scale_s,
-                         const float *v, float *m, float *params, float lr, float eps,
-                         hipStream_t s);
+void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s);
+void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStream_t s);
+void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s);
 
 }  // namespace ob

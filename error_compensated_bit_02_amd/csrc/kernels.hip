@@ -11,15 +11,27 @@
 // accumulation.  Nothing here is a dense contraction, so there is no MFMA.
 //
 // Element mapping.  A workgroup of 4 wavefronts handles one tile of up to
-// 8192 elements of one tensor; wavefront v owns elements [2048 v, 2048 v +
-// 2048) of the tile and lane l owns element 64 c + l of that range for
-// c = 0..31.  Every load and store of one c is a contiguous 256-byte wave
-// access, and __ballot over one c is directly the packed sign word (bit l =
-// element 64 c + l), so packing costs one compare per element.
+// kTile elements of one tensor; wavefront v owns elements [v kSub, (v+1) kSub)
+// of the tile and lane l owns element 64 c + l of that range for
+// c < kPerLane.  Every load and store of one c is a contiguous 256-byte
+// wavefront access, and __ballot over one c is directly the packed sign word
+// (bit l = element 64 c + l), so packing costs one compare per element.
+// Sums of squares are reduced per wavefront, parked in LDS, folded per tile
+// in a fixed order (two barriers per tile, none per worker) and per tensor by
+// scale_finalize.
+//
+// Two forms of the state between steps:
+//   strict    err_w / err_s hold the errors and m the momentum (two passes
+//             per phase: the error needs the whole-tensor scale);
+//   residual  err_w / err_s hold the values that were compressed (x, z) and
+//             the scales of that step; the error x - s*sign(x) is formed,
+//             exactly as the strict form stores it, when the next step reads
+//             it, and the momentum is the server message (+-s_s per sign bit),
+//             which it equals exactly.  One pass per phase.
 //
 // Floating point.  fp32 products and sums are written as separate operations
-// and the file is compiled without contraction, so each rounds once, as the
-// method's readings require; fp32 sqrt and division are correctly rounded.
+// and the file is compiled without contraction, so each rounds once; fp32
+// sqrt and division are correctly rounded.
 #include "internal.h"
 
 #pragma clang fp contract(off)
@@ -27,6 +39,9 @@
 namespace ob {
 namespace {
 
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
 template <typename G>
 __device__ __forceinline__ float grad_value(const G *p);
 
@@ -71,36 +86,54 @@ __device__ __forceinline__ void dd_wave_reduce(double &hi, double &lo) {
   }
 }
 
-// Sum the four wavefronts' pairs in a fixed order and store one partial.
-// red is a [kWaves] LDS slot owned by this call; the caller alternates two
-// slots so one barrier per call suffices.
-__device__ __forceinline__ void dd_block_store(double hi, double lo, double2 *red, double2 *out) {
+// Per-tile partial sums: each wavefront parks its reduced pair for row r in
+// red[r % kFlushRows][wave]; every kFlushRows rows (and after the last) the
+// workgroup folds the four wavefronts' pairs in a fixed order and stores one
+// partial per (row, tile).  Two barriers per flush, none per row otherwise.
+constexpr int kFlushRows = 32;
+
+struct PartialSink {
+  double2 (*red)[kWaves];
+  double2 *partials;   // row-major [rows][num_tiles]
+  int num_tiles;
+};
+
+__device__ __forceinline__ void park_partial(const PartialSink &ps, int slot, int wave, double hi,
+                                             double lo) {
   dd_wave_reduce(hi, lo);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = make_double2(hi, lo);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double h = red[0].x, l = red[0].y;
-#pragma unroll
-    for (int v = 1; v < kWaves; ++v) dd_add(h, l, red[v].x, red[v].y);
-    *out = make_double2(h, l);
-  }
+  if ((threadIdx.x & 63) == 0) ps.red[slot][wave] = make_double2(hi, lo);
 }
 
+// Rows [row0, row0 + nrows) parked in slots [0, nrows); workgroup-uniform call.
+__device__ __forceinline__ void flush_partials(const PartialSink &ps, int row0, int nrows) {
+  __syncthreads();
+  if (static_cast<int>(threadIdx.x) < nrows) {
+    const int r = threadIdx.x;
+    double h = ps.red[r][0].x, l = ps.red[r][0].y;
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) dd_add(h, l, ps.red[r][v].x, ps.red[r][v].y);
+    ps.partials[static_cast<size_t>(row0 + r) * ps.num_tiles + blockIdx.x] = make_double2(h, l);
+  }
+  __syncthreads();
+}
+
+// x - s*sign(x) with sign(x) = +1 for x >= 0: the error left by a 1-bit code.
+__device__ __forceinline__ float onebit_error(float x, float s) { return x >= 0.0f ? x - s : x + s; }
+
 struct Lanes {
-  int lane;     // 0..63
-  int sub0;     // first element of this wavefront within the tile
-  int64_t base; // flat index of that element
-  int nwords;   // sign words of this wavefront that fall inside the tile
+  int lane;      // 0..63
+  int wave;      // 0..kWaves-1 (wavefront-uniform)
+  int sub0;      // first element of this wavefront within the tile
+  int64_t base;  // flat index of that element
+  int nwords;    // sign words of this wavefront that fall inside the tile
 };
 
 template <bool kFull>
 __device__ __forceinline__ Lanes lanes_of(const Tile &tl) {
   Lanes r;
   r.lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  r.sub0 = wave * kSub;
+  r.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  r.sub0 = r.wave * kSub;
   r.base = tl.start + r.sub0;
   if (kFull) {
     r.nwords = kPerLane;
@@ -116,114 +149,105 @@ __device__ __forceinline__ bool in_tile(const Tile &tl, const Lanes &ln, int c) 
   return kFull || (ln.sub0 + 64 * c + ln.lane < tl.len);
 }
 
-// ---------------------------------------------------------------------------
-// worker pass 1: x = (c1*m + c2*g) + e, sign words, per-tile sum of x^2
-// ---------------------------------------------------------------------------
-template <typename G, bool kFull>
-__device__ __forceinline__ void worker_pass1_tile(const Tile &tl, const G *__restrict__ grads,
-                                                  const float *__restrict__ m,
-                                                  const float *__restrict__ err_w,
-                                                  uint64_t *__restrict__ packed_w,
-                                                  double2 *__restrict__ partials, int64_t N,
-                                                  int64_t Nw, int num_tiles, int w0, int w1,
-                                                  float c1, float c2, double2 *red) {
-  const Lanes ln = lanes_of<kFull>(tl);
-  float mr[kPerLane];
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c)
-    mr[c] = in_tile<kFull>(tl, ln, c) ? m[ln.base + 64 * c + ln.lane] : 0.0f;
+// Sign words of one packed row for this wavefront: lane j < nwords holds word
+// j (one coalesced load); word c is broadcast from lane c by readlane.
+template <bool kFull>
+__device__ __forceinline__ uint64_t load_words(const uint64_t *row, const Lanes &ln) {
+  return (kFull ? ln.lane < kPerLane : ln.lane < ln.nwords) ? row[ln.lane] : 0ull;
+}
 
-  for (int w = w0; w < w1; ++w) {
-    const G *gw = grads + static_cast<size_t>(w) * N + ln.base + ln.lane;
-    const float *ew = err_w + static_cast<size_t>(w) * N + ln.base + ln.lane;
-    float gv[kPerLane], ev[kPerLane];
+// +-s for this lane's element 64 c + lane, from the words held by load_words.
+__device__ __forceinline__ float signed_scale(uint64_t words, int c, int lane, float s) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(words)), c);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(words >> 32)), c);
+  const uint32_t half = lane < 32 ? lo : hi;
+  return ((half >> (lane & 31)) & 1u) ? s : -s;
+}
+
+// ---------------------------------------------------------------------------
+// worker kernels
+//   kPass1       strict: x = (c1*m + c2*g) + e; signs; sum of x^2
+//   kPass2       strict: recompute x; e = x - s*sign(x)
+//   kResidFirst  residual, first step: as kPass1 from stored e and m, and x is stored
+//   kResid       residual: e = x_prev - s_prev*sign(x_prev), m = previous server
+//                message; then as kResidFirst
+// ---------------------------------------------------------------------------
+enum { kPass1 = 0, kPass2 = 1, kResidFirst = 2, kResid = 3 };
+
+template <int kMode, typename G, bool kFull>
+__device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, const WorkerArgs &a,
+                                            const PartialSink &sink) {
+  const Lanes ln = lanes_of<kFull>(tl);
+  const int t = tl.tensor;
+  float mr[kPerLane];
+  if (kMode == kResid) {
+    const float ss = a.scale_s[t];
+    const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c)
+      mr[c] = in_tile<kFull>(tl, ln, c) ? signed_scale(words, c, ln.lane, ss) : 0.0f;
+  } else {
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c)
+      mr[c] = in_tile<kFull>(tl, ln, c) ? a.m[ln.base + 64 * c + ln.lane] : 0.0f;
+  }
+
+  const G *grads = static_cast<const G *>(a.grads) + ln.base + ln.lane;
+  float gv[kPerLane], ev[kPerLane];
+  auto load = [&](int w, float *gdst, float *edst) {
+    const G *gw = grads + static_cast<size_t>(w) * g.N;
+    const float *ew = a.err_w + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
       const bool ok = in_tile<kFull>(tl, ln, c);
-      gv[c] = ok ? grad_value(gw + 64 * c) : 0.0f;
-      ev[c] = ok ? ew[64 * c] : 0.0f;
+      gdst[c] = ok ? grad_value(gw + 64 * c) : 0.0f;
+      edst[c] = ok ? ew[64 * c] : 0.0f;
+    }
+  };
+  for (int w = a.w0; w < a.w1; ++w) {
+    float *ew = a.err_w + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
+    // kPass2: this step's scale; kResid: the previous step's scale
+    const float s = (kMode == kPass2 || kMode == kResid) ? a.scale_w[static_cast<size_t>(w) * g.T + t] : 0.0f;
+    load(w, gv, ev);
+    if (kMode == kPass2) {
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const float mw = a.c1 * mr[c] + a.c2 * gv[c];
+        const float x = mw + ev[c];
+        if (in_tile<kFull>(tl, ln, c)) ew[64 * c] = onebit_error(x, s);
+      }
+      continue;
     }
     double hi = 0.0, lo = 0.0;
     uint64_t word = 0;
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
-      const float mw = c1 * mr[c] + c2 * gv[c];
-      const float x = mw + ev[c];
-      const uint64_t bal = __ballot(in_tile<kFull>(tl, ln, c) && x >= 0.0f);
+      const bool ok = in_tile<kFull>(tl, ln, c);
+      const float e = (kMode == kResid) ? onebit_error(ev[c], s) : ev[c];
+      const float mw = a.c1 * mr[c] + a.c2 * gv[c];
+      const float x = ok ? mw + e : 0.0f;
+      const uint64_t bal = __ballot(ok && x >= 0.0f);
       if (ln.lane == c) word = bal;
       dd_accumulate(hi, lo, x);  // lanes outside the tile hold x = 0 and add nothing
+      if (kMode != kPass1 && ok) ew[64 * c] = x;
     }
     if (ln.lane < ln.nwords)
-      packed_w[static_cast<size_t>(w) * Nw + (ln.base >> 6) + ln.lane] = word;
-    dd_block_store(hi, lo, red + (w & 1) * kWaves,
-                   partials + static_cast<size_t>(w) * num_tiles + blockIdx.x);
+      a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane] = word;
+    const int slot = (w - a.w0) % kFlushRows;
+    park_partial(sink, slot, ln.wave, hi, lo);
+    if (slot == kFlushRows - 1 || w == a.w1 - 1) flush_partials(sink, w - slot, slot + 1);
   }
 }
 
-template <typename G>
-__global__ __launch_bounds__(kBlock) void worker_pass1(Geometry g, const G *__restrict__ grads,
-                                                       const float *__restrict__ m,
-                                                       const float *__restrict__ err_w,
-                                                       uint64_t *__restrict__ packed_w,
-                                                       double2 *__restrict__ partials, int w0,
-                                                       int w1, float c1, float c2) {
-  __shared__ double2 red[2 * kWaves];
+template <typename G, int kMode>
+__global__ __launch_bounds__(kBlock) void worker_kernel(Geometry g, WorkerArgs a) {
+  __shared__ double2 red[kFlushRows][kWaves];
+  const PartialSink sink{red, a.partials, g.num_tiles};
   const Tile tl = g.tiles[blockIdx.x];
   if (tl.len == kTile)
-    worker_pass1_tile<G, true>(tl, grads, m, err_w, packed_w, partials, g.N, g.Nw, g.num_tiles,
-                               w0, w1, c1, c2, red);
+    worker_tile<kMode, G, true>(tl, g, a, sink);
   else
-    worker_pass1_tile<G, false>(tl, grads, m, err_w, packed_w, partials, g.N, g.Nw, g.num_tiles,
-                                w0, w1, c1, c2, red);
-}
-
-// ---------------------------------------------------------------------------
-// worker pass 2: recompute x, store e = x - s*sign(x)
-// ---------------------------------------------------------------------------
-template <typename G, bool kFull>
-__device__ __forceinline__ void worker_pass2_tile(const Tile &tl, const G *__restrict__ grads,
-                                                  const float *__restrict__ m,
-                                                  float *__restrict__ err_w,
-                                                  const float *__restrict__ scale_w, int64_t N,
-                                                  int T, int w0, int w1, float c1, float c2) {
-  const Lanes ln = lanes_of<kFull>(tl);
-  float mr[kPerLane];
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c)
-    mr[c] = in_tile<kFull>(tl, ln, c) ? m[ln.base + 64 * c + ln.lane] : 0.0f;
-
-  for (int w = w0; w < w1; ++w) {
-    const float s = scale_w[static_cast<size_t>(w) * T + tl.tensor];
-    const G *gw = grads + static_cast<size_t>(w) * N + ln.base + ln.lane;
-    float *ew = err_w + static_cast<size_t>(w) * N + ln.base + ln.lane;
-    float gv[kPerLane], ev[kPerLane];
-#pragma unroll
-    for (int c = 0; c < kPerLane; ++c) {
-      const bool ok = in_tile<kFull>(tl, ln, c);
-      gv[c] = ok ? grad_value(gw + 64 * c) : 0.0f;
-      ev[c] = ok ? ew[64 * c] : 0.0f;
-    }
-#pragma unroll
-    for (int c = 0; c < kPerLane; ++c) {
-      const float mw = c1 * mr[c] + c2 * gv[c];
-      const float x = mw + ev[c];
-      const float e = x >= 0.0f ? x - s : x + s;
-      if (in_tile<kFull>(tl, ln, c)) ew[64 * c] = e;
-    }
-  }
-}
-
-template <typename G>
-__global__ __launch_bounds__(kBlock) void worker_pass2(Geometry g, const G *__restrict__ grads,
-                                                       const float *__restrict__ m,
-                                                       float *__restrict__ err_w,
-                                                       const float *__restrict__ scale_w, int w0,
-                                                       int w1, float c1, float c2) {
-  const Tile tl = g.tiles[blockIdx.x];
-  if (tl.len == kTile)
-    worker_pass2_tile<G, true>(tl, grads, m, err_w, scale_w, g.N, g.T, w0, w1, c1, c2);
-  else
-    worker_pass2_tile<G, false>(tl, grads, m, err_w, scale_w, g.N, g.T, w0, w1, c1, c2);
+    worker_tile<kMode, G, false>(tl, g, a, sink);
 }
 
 // ---------------------------------------------------------------------------
@@ -240,11 +264,17 @@ __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
   const int t = static_cast<int>(id % g.T);
   const double2 *row = partials + static_cast<size_t>(row0 + r) * g.num_tiles;
   double hi = 0.0, lo = 0.0;
-  for (int i = g.tile_begin[t] + lane; i < g.tile_begin[t + 1]; i += 64) {
+  const int end = g.tile_begin[t + 1];
+  for (int i = g.tile_begin[t] + lane; i < end; i += 64) {
     const double2 p = row[i];
     dd_add(hi, lo, p.x, p.y);
   }
-  dd_wave_reduce(hi, lo);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const double oh = __shfl_xor(hi, d);
+    const double ol = __shfl_xor(lo, d);
+    dd_add(hi, lo, oh, ol);
+  }
   if (lane == 0) {
     const double S = hi + lo;                          // fl64 of the sum of squares
     const double q = S / static_cast<double>(g.numel[t]);
@@ -253,62 +283,89 @@ __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
 }
 
 // ---------------------------------------------------------------------------
-// server: y = (ascending sum of +-s_w) / W, z = y + e_s
-//   kMode 0: per-tile sum of z^2
-//   kMode 1: sign words of z, e_s = z - s_s*sign(z)
-//   kMode 2: kMode 1 plus m = s_s*sign(z) and the frozen-variance update
+// server kernels: y = (ascending sum over w of +-s_w) / W, z = y + e_s
+//   kS1          strict: sum of z^2
+//   kS2          strict: sign words of z; e_s = z - s_s*sign(z)
+//   kS2Update    kS2 plus m = s_s*sign(z) and the frozen-variance update
+//   kSResidFirst residual, first step: z from the stored e_s; store z, sign words, sum of z^2
+//   kSResid      residual: e_s = z_prev - s_s,prev*sign(z_prev); then as kSResidFirst
 // ---------------------------------------------------------------------------
-template <bool kFull, int kMode>
-__device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g,
-                                            const uint64_t *__restrict__ packed_w,
-                                            const float *__restrict__ scale_w,
-                                            float *__restrict__ err_s,
-                                            double2 *__restrict__ partials,
-                                            const float *__restrict__ scale_s,
-                                            uint64_t *__restrict__ packed_s,
-                                            const float *__restrict__ v, float *__restrict__ m,
-                                            float *__restrict__ params, float lr, float eps,
-                                            double2 *red) {
+enum { kS1 = 0, kS2 = 1, kS2Update = 2, kSResidFirst = 3, kSResid = 4 };
+
+template <int kMode, bool kFull, bool kPow2>
+__device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, const ServerArgs &a,
+                                            const PartialSink &sink) {
   const Lanes ln = lanes_of<kFull>(tl);
+  const int t = tl.tensor;
   float acc[kPerLane];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) acc[c] = 0.0f;
-  const uint64_t *pw = packed_w + (ln.base >> 6);
-  for (int w = 0; w < g.W; ++w) {
-    const float s = scale_w[static_cast<size_t>(w) * g.T + tl.tensor];
-    const uint64_t *row = pw + static_cast<size_t>(w) * g.Nw;
+  const uint64_t *pw = a.packed_w + (ln.base >> 6);
+  // workers in groups of 8: the group's word loads are issued together, then
+  // summed in ascending worker order
+  constexpr int kGroup = 8;
+  for (int w0 = 0; w0 < g.W; w0 += kGroup) {
+    uint64_t words[kGroup];
+    float sw[kGroup];
 #pragma unroll
-    for (int c = 0; c < kPerLane; ++c) {
-      const uint64_t word = (kFull || c < ln.nwords) ? row[c] : 0ull;
-      const bool bit = (word >> ln.lane) & 1ull;
-      acc[c] = acc[c] + (bit ? s : -s);
+    for (int j = 0; j < kGroup; ++j) {
+      const bool live = w0 + j < g.W;
+      words[j] = live ? load_words<kFull>(pw + static_cast<size_t>(w0 + j) * g.Nw, ln) : 0ull;
+      sw[j] = live ? a.scale_w[static_cast<size_t>(w0 + j) * g.T + t] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      if (w0 + j >= g.W) break;
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) acc[c] = acc[c] + signed_scale(words[j], c, ln.lane, sw[j]);
     }
   }
   const float wf = static_cast<float>(g.W);
-  float *es = err_s + ln.base + ln.lane;
+  const float inv_w = 1.0f / wf;   // exact when W is a power of two
+  float *es = a.err_s + ln.base + ln.lane;
+  // kS2/kS2Update: this step's server scale; kSResid: the previous step's
+  const float ss = (kMode == kS2 || kMode == kS2Update || kMode == kSResid) ? a.scale_s[t] : 0.0f;
   float z[kPerLane];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     const bool ok = in_tile<kFull>(tl, ln, c);
-    const float e_old = ok ? es[64 * c] : 0.0f;
-    z[c] = ok ? acc[c] / wf + e_old : 0.0f;
+    const float stored = ok ? es[64 * c] : 0.0f;
+    const float e_old = (kMode == kSResid) ? onebit_error(stored, ss) : stored;
+    // for W = 2^k, acc * 2^-k is the correctly rounded quotient, as the division is
+    const float y = kPow2 ? acc[c] * inv_w : acc[c] / wf;
+    z[c] = ok ? y + e_old : 0.0f;
   }
-  if (kMode == 0) {
+  if (kMode == kS1) {
     double hi = 0.0, lo = 0.0;
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) dd_accumulate(hi, lo, z[c]);
-    dd_block_store(hi, lo, red, partials + static_cast<size_t>(g.W) * g.num_tiles + blockIdx.x);
+    park_partial(sink, 0, ln.wave, hi, lo);
+    flush_partials(sink, g.W, 1);
     return;
   }
-  const float ss = scale_s[tl.tensor];
   uint64_t word = 0;
-  float vv[kPerLane], pv[kPerLane];
-  if (kMode == 2) {
+  if (kMode == kSResidFirst || kMode == kSResid) {
+    double hi = 0.0, lo = 0.0;
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
       const bool ok = in_tile<kFull>(tl, ln, c);
-      vv[c] = ok ? v[ln.base + 64 * c + ln.lane] : 0.0f;
-      pv[c] = ok ? params[ln.base + 64 * c + ln.lane] : 0.0f;
+      const uint64_t bal = __ballot(ok && z[c] >= 0.0f);
+      if (ln.lane == c) word = bal;
+      dd_accumulate(hi, lo, z[c]);
+      if (ok) es[64 * c] = z[c];
+    }
+    if (ln.lane < ln.nwords) a.packed_s[(ln.base >> 6) + ln.lane] = word;
+    park_partial(sink, 0, ln.wave, hi, lo);
+    flush_partials(sink, g.W, 1);
+    return;
+  }
+  float vv[kPerLane], pv[kPerLane];
+  if (kMode == kS2Update) {
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c) {
+      const bool ok = in_tile<kFull>(tl, ln, c);
+      vv[c] = ok ? a.v[ln.base + 64 * c + ln.lane] : 0.0f;
+      pv[c] = ok ? a.params[ln.base + 64 * c + ln.lane] : 0.0f;
     }
   }
 #pragma unroll
@@ -319,71 +376,111 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g,
     if (ln.lane == c) word = bal;
     if (ok) {
       es[64 * c] = bit ? z[c] - ss : z[c] + ss;
-      if (kMode == 2) {
+      if (kMode == kS2Update) {
         const float mv = bit ? ss : -ss;
-        const float d = __builtin_sqrtf(vv[c]) + eps;
+        const float d = __builtin_sqrtf(vv[c]) + a.eps;
         const float u = mv / d;
-        m[ln.base + 64 * c + ln.lane] = mv;
-        params[ln.base + 64 * c + ln.lane] = pv[c] - lr * u;
+        a.m[ln.base + 64 * c + ln.lane] = mv;
+        a.params[ln.base + 64 * c + ln.lane] = pv[c] - a.lr * u;
       }
     }
   }
-  if (ln.lane < ln.nwords) packed_s[(ln.base >> 6) + ln.lane] = word;
+  if (ln.lane < ln.nwords) a.packed_s[(ln.base >> 6) + ln.lane] = word;
 }
 
-template <int kMode>
-__global__ __launch_bounds__(kBlock) void server_kernel(
-    Geometry g, const uint64_t *__restrict__ packed_w, const float *__restrict__ scale_w,
-    float *__restrict__ err_s, double2 *__restrict__ partials, const float *__restrict__ scale_s,
-    uint64_t *__restrict__ packed_s, const float *__restrict__ v, float *__restrict__ m,
-    float *__restrict__ params, float lr, float eps) {
-  __shared__ double2 red[kWaves];
+template <int kMode, bool kPow2>
+__global__ __launch_bounds__(kBlock) void server_kernel(Geometry g, ServerArgs a) {
+  __shared__ double2 red[1][kWaves];
+  const PartialSink sink{red, a.partials, g.num_tiles};
   const Tile tl = g.tiles[blockIdx.x];
   if (tl.len == kTile)
-    server_tile<true, kMode>(tl, g, packed_w, scale_w, err_s, partials, scale_s, packed_s, v, m,
-                             params, lr, eps, red);
+    server_tile<kMode, true, kPow2>(tl, g, a, sink);
   else
-    server_tile<false, kMode>(tl, g, packed_w, scale_w, err_s, partials, scale_s, packed_s, v, m,
-                              params, lr, eps, red);
+    server_tile<kMode, false, kPow2>(tl, g, a, sink);
 }
 
 // ---------------------------------------------------------------------------
-// update from a server message: m = s_s*sign, p -= lr * m / (sqrt(v) + eps)
+// update from a server message: m = s_s*sign (stored if kStoreM),
+// p <- p - lr * (m / (sqrt(v) + eps))
 // ---------------------------------------------------------------------------
-template <bool kFull>
-__device__ __forceinline__ void apply_tile(const Tile &tl, const uint64_t *__restrict__ packed_s,
-                                           const float *__restrict__ scale_s,
-                                           const float *__restrict__ v, float *__restrict__ m,
-                                           float *__restrict__ params, float lr, float eps) {
+template <bool kStoreM, bool kFull>
+__device__ __forceinline__ void update_tile(const Tile &tl, const UpdateArgs &a) {
   const Lanes ln = lanes_of<kFull>(tl);
-  const float ss = scale_s[tl.tensor];
-  const uint64_t *ps = packed_s + (ln.base >> 6);
+  const float ss = a.scale_s[tl.tensor];
+  const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
+  float vv[kPerLane], pv[kPerLane];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
+    const bool ok = in_tile<kFull>(tl, ln, c);
+    vv[c] = ok ? a.v[ln.base + 64 * c + ln.lane] : 0.0f;
+    pv[c] = ok ? a.params[ln.base + 64 * c + ln.lane] : 0.0f;
+  }
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    const float mv = signed_scale(words, c, ln.lane, ss);  // every lane takes part in the broadcast
     if (!in_tile<kFull>(tl, ln, c)) continue;
-    const uint64_t word = ps[c];
-    const bool bit = (word >> ln.lane) & 1ull;
     const int64_t i = ln.base + 64 * c + ln.lane;
-    const float mv = bit ? ss : -ss;
-    const float d = __builtin_sqrtf(v[i]) + eps;
+    const float d = __builtin_sqrtf(vv[c]) + a.eps;
     const float u = mv / d;
-    m[i] = mv;
-    params[i] = params[i] - lr * u;
+    if (kStoreM) a.m[i] = mv;
+    a.params[i] = pv[c] - a.lr * u;
   }
 }
 
-__global__ __launch_bounds__(kBlock) void apply_update(Geometry g,
-                                                       const uint64_t *__restrict__ packed_s,
-                                                       const float *__restrict__ scale_s,
-                                                       const float *__restrict__ v,
-                                                       float *__restrict__ m,
-                                                       float *__restrict__ params, float lr,
-                                                       float eps) {
+template <bool kStoreM>
+__global__ __launch_bounds__(kBlock) void update_kernel(Geometry g, UpdateArgs a) {
   const Tile tl = g.tiles[blockIdx.x];
   if (tl.len == kTile)
-    apply_tile<true>(tl, packed_s, scale_s, v, m, params, lr, eps);
+    update_tile<kStoreM, true>(tl, a);
   else
-    apply_tile<false>(tl, packed_s, scale_s, v, m, params, lr, eps);
+    update_tile<kStoreM, false>(tl, a);
+}
+
+// ---------------------------------------------------------------------------
+// materialize: residual form -> errors and momentum
+//   e_w = x_w - s_w*sign(x_w), e_s = z - s_s*sign(z), m = s_s*sign(z).
+// Outputs may alias the inputs (each element is read, then written, by one lane).
+// ---------------------------------------------------------------------------
+template <bool kFull>
+__device__ __forceinline__ void materialize_tile(const Tile &tl, const Geometry &g,
+                                                 const MaterializeArgs &a) {
+  const Lanes ln = lanes_of<kFull>(tl);
+  const int t = tl.tensor;
+  for (int w = 0; w < g.W; ++w) {
+    const float s = a.scale_w[static_cast<size_t>(w) * g.T + t];
+    const size_t off = static_cast<size_t>(w) * g.N + ln.base + ln.lane;
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c)
+      if (in_tile<kFull>(tl, ln, c)) a.e_w[off + 64 * c] = onebit_error(a.x_w[off + 64 * c], s);
+  }
+  const float ss = a.scale_s[t];
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    if (!in_tile<kFull>(tl, ln, c)) continue;
+    const int64_t i = ln.base + 64 * c + ln.lane;
+    const float z = a.z[i];
+    a.e_s[i] = onebit_error(z, ss);
+    a.m[i] = z >= 0.0f ? ss : -ss;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void materialize_kernel(Geometry g, MaterializeArgs a) {
+  const Tile tl = g.tiles[blockIdx.x];
+  if (tl.len == kTile)
+    materialize_tile<true>(tl, g, a);
+  else
+    materialize_tile<false>(tl, g, a);
+}
+
+template <typename G>
+void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStream_t s) {
+  const dim3 grid(g.num_tiles), block(kBlock);
+  switch (mode) {
+    case kPass1: hipLaunchKernelGGL((worker_kernel<G, kPass1>), grid, block, 0, s, g, a); break;
+    case kPass2: hipLaunchKernelGGL((worker_kernel<G, kPass2>), grid, block, 0, s, g, a); break;
+    case kResidFirst: hipLaunchKernelGGL((worker_kernel<G, kResidFirst>), grid, block, 0, s, g, a); break;
+    default: hipLaunchKernelGGL((worker_kernel<G, kResid>), grid, block, 0, s, g, a); break;
+  }
 }
 
 }  // namespace
@@ -391,18 +488,14 @@ __global__ __launch_bounds__(kBlock) void apply_update(Geometry g,
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-void launch_worker_pass1(const Geometry &g, bool bf16, int w0, int w1, const void *grads,
-                         const float *m, const float *err_w, uint64_t *packed_w,
-                         double2 *partials, float c1, float c2, hipStream_t s) {
-  const dim3 grid(g.num_tiles), block(kBlock);
+void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s) {
+  const int mode = pass == WorkerPass::kStrictSigns ? kPass1
+                 : pass == WorkerPass::kStrictErrors ? kPass2
+                 : pass == WorkerPass::kResidualFirst ? kResidFirst : kResid;
   if (bf16)
-    hipLaunchKernelGGL(worker_pass1<uint16_t>, grid, block, 0, s, g,
-                       static_cast<const uint16_t *>(grads), m, err_w, packed_w, partials, w0, w1,
-                       c1, c2);
+    launch_worker_mode<uint16_t>(mode, g, a, s);
   else
-    hipLaunchKernelGGL(worker_pass1<float>, grid, block, 0, s, g,
-                       static_cast<const float *>(grads), m, err_w, packed_w, partials, w0, w1, c1,
-                       c2);
+    launch_worker_mode<float>(mode, g, a, s);
 }
 
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0, int nrows,
@@ -412,43 +505,40 @@ void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0,
   hipLaunchKernelGGL(scale_finalize, grid, block, 0, s, g, partials, row0, nrows, out);
 }
 
-void launch_worker_pass2(const Geometry &g, bool bf16, int w0, int w1, const void *grads,
-                         const float *m, float *err_w, const float *scale_w, float c1, float c2,
-                         hipStream_t s) {
+template <bool kPow2>
+void launch_server_w(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s) {
   const dim3 grid(g.num_tiles), block(kBlock);
-  if (bf16)
-    hipLaunchKernelGGL(worker_pass2<uint16_t>, grid, block, 0, s, g,
-                       static_cast<const uint16_t *>(grads), m, err_w, scale_w, w0, w1, c1, c2);
+  switch (pass) {
+    case ServerPass::kStrictSums:
+      hipLaunchKernelGGL((server_kernel<kS1, kPow2>), grid, block, 0, s, g, a); break;
+    case ServerPass::kStrictErrors:
+      hipLaunchKernelGGL((server_kernel<kS2, kPow2>), grid, block, 0, s, g, a); break;
+    case ServerPass::kStrictErrorsUpdate:
+      hipLaunchKernelGGL((server_kernel<kS2Update, kPow2>), grid, block, 0, s, g, a); break;
+    case ServerPass::kResidualFirst:
+      hipLaunchKernelGGL((server_kernel<kSResidFirst, kPow2>), grid, block, 0, s, g, a); break;
+    case ServerPass::kResidual:
+      hipLaunchKernelGGL((server_kernel<kSResid, kPow2>), grid, block, 0, s, g, a); break;
+  }
+}
+
+void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s) {
+  if ((g.W & (g.W - 1)) == 0)
+    launch_server_w<true>(pass, g, a, s);
   else
-    hipLaunchKernelGGL(worker_pass2<float>, grid, block, 0, s, g,
-                       static_cast<const float *>(grads), m, err_w, scale_w, w0, w1, c1, c2);
+    launch_server_w<false>(pass, g, a, s);
 }
 
-void launch_server_pass1(const Geometry &g, const uint64_t *packed_w, const float *scale_w,
-                         const float *err_s, double2 *partials, hipStream_t s) {
-  hipLaunchKernelGGL(server_kernel<0>, dim3(g.num_tiles), dim3(kBlock), 0, s, g, packed_w,
-                     scale_w, const_cast<float *>(err_s), partials, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, 0.0f, 0.0f);
-}
-
-void launch_server_pass2(const Geometry &g, bool update, const uint64_t *packed_w,
-                         const float *scale_w, float *err_s, const float *scale_s,
-                         uint64_t *packed_s, const float *v, float *m, float *params, float lr,
-                         float eps, hipStream_t s) {
-  if (update)
-    hipLaunchKernelGGL(server_kernel<2>, dim3(g.num_tiles), dim3(kBlock), 0, s, g, packed_w,
-                       scale_w, err_s, nullptr, scale_s, packed_s, v, m, params, lr, eps);
+void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStream_t s) {
+  const dim3 grid(g.num_tiles), block(kBlock);
+  if (store_m)
+    hipLaunchKernelGGL(update_kernel<true>, grid, block, 0, s, g, a);
   else
-    hipLaunchKernelGGL(server_kernel<1>, dim3(g.num_tiles), dim3(kBlock), 0, s, g, packed_w,
-                       scale_w, err_s, nullptr, scale_s, packed_s, nullptr, nullptr, nullptr, 0.0f,
-                       0.0f);
+    hipLaunchKernelGGL(update_kernel<false>, grid, block, 0, s, g, a);
 }
 
-void launch_apply_update(const Geometry &g, const uint64_t *packed_s, const float *scale_s,
-                         const float *v, float *m, float *params, float lr, float eps,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(apply_update, dim3(g.num_tiles), dim3(kBlock), 0, s, g, packed_s, scale_s, v,
-                     m, params, lr, eps);
+void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(materialize_kernel, dim3(g.num_tiles), dim3(kBlock), 0, s, g, a);
 }
 
 }  // namespace ob

@@ -129,6 +129,38 @@ int ob_step(ob_ctx *ctx, const void *grads, float *m, const float *v, float *par
             float *err_w, float *err_s, uint64_t *packed_w, float *scale_w,
             uint64_t *packed_s, float *scale_s, double lr, void *stream);
 
+/* The same step with the error and momentum state kept in residual form,
+ * one pass per phase instead of two.
+ *
+ * Residual form: err_w[w] holds x_w, the value worker w compressed in the
+ * last step, and scale_w its scales; err_s holds z, the value the server
+ * compressed, and scale_s / packed_s its scales and message.  The state of
+ * the strict form is an exact function of it (see ob_materialize):
+ *   e_w = x_w - s_w,t*sign(x_w),  e_s = z - s_s,t*sign(z),  m = s_s,t*sign(z),
+ * the same fp32 operations the strict form performs, so both forms follow
+ * bit-identical trajectories (the momentum of this phase is the server's
+ * 1-bit message, so it needs no separate buffer).
+ *
+ *   first != 0: err_w, err_s and m hold strict-form errors and momentum (for
+ *               example zeros at the start of the compression phase);
+ *               packed_s and scale_s are only written.
+ *   first == 0: the buffers hold the residual form left by the previous call;
+ *               m is not read and may be NULL.
+ * On return err_w, err_s, packed_w, scale_w, packed_s and scale_s hold this
+ * step's residual form and messages, params is updated, m is untouched. */
+int ob_step_residual(ob_ctx *ctx, int32_t first, const void *grads, const float *m,
+                     const float *v, float *params, float *err_w, float *err_s,
+                     uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s,
+                     double lr, void *stream);
+
+/* Writes the strict-form state of a residual-form state:
+ *   err_w [W][N] = x_w - s_w,t*sign(x_w),  err_s [N] = z - s_s,t*sign(z),
+ *   m [N] = s_s,t*sign(z).
+ * x_w [W][N], scale_w [W][T], z [N], scale_s [T] are read.  Outputs may be
+ * the same buffers as the inputs (in place). */
+int ob_materialize(ob_ctx *ctx, const float *x_w, const float *scale_w, const float *z,
+                   const float *scale_s, float *err_w, float *err_s, float *m, void *stream);
+
 /* Kernel timing for measurement.  With profiling on, every kernel the context
  * launches is bracketed by HIP events on its stream.  ob_profile_read waits for
  * the recorded events, writes per kernel kind the summed milliseconds and the

@@ -103,6 +103,23 @@ class Run:
         self.ctx.apply_update(b["packed_s"], b["scale_s"], s["v"], s["m"], s["p"],
                               self.wl.lr if lr is None else lr)
 
+    def step_residual(self, grads: torch.Tensor, first: bool, lr: Optional[float] = None) -> None:
+        """The same step with err_w / err_s kept in residual form."""
+        s, b = self.state, self.bufs
+        self.ctx.step_residual(first, grads, s["m"], s["v"], s["p"], s["err_w"], s["err_s"],
+                               b["packed_w"], b["scale_w"], b["packed_s"], b["scale_s"],
+                               self.wl.lr if lr is None else lr)
+
+    def materialized(self) -> Dict[str, torch.Tensor]:
+        """Strict-form state of a residual-form run, in fresh zero-filled buffers
+        (padding is never written, so it stays zero as in the strict form)."""
+        s, b = self.state, self.bufs
+        out = {"p": s["p"], "v": s["v"], "err_w": torch.zeros_like(s["err_w"]),
+               "err_s": torch.zeros_like(s["err_s"]), "m": torch.zeros_like(s["m"])}
+        self.ctx.materialize(s["err_w"], b["scale_w"], s["err_s"], b["scale_s"], out["err_w"],
+                             out["err_s"], out["m"])
+        return out
+
     def host_state(self, tensors: Sequence[int]) -> List[ob.TensorState]:
         """Per-tensor host copies (for seeding the oracle with the same initial values)."""
         out = []
@@ -114,12 +131,14 @@ class Run:
                                       host_slice(s["err_w"], lo, hi)))
         return out
 
-    def compare(self, t: int, out: ob.StepOutput, rep: Report, what: str) -> None:
-        """Compare tensor t's device state and messages with one oracle step output."""
+    def compare(self, t: int, out: ob.StepOutput, rep: Report, what: str,
+                state: Optional[Dict[str, torch.Tensor]] = None) -> None:
+        """Compare tensor t's device state (default: this run's buffers) and
+        messages with one oracle step output."""
         wl, off = self.wl, self.off
         lo, hi = off[t], off[t] + wl.numel[t]
         wlo, whi = off[t] // 64, off[t] // 64 + (wl.numel[t] + 63) // 64
-        s, b = self.state, self.bufs
+        s, b = (self.state if state is None else state), self.bufs
         ref_w, ref_sw = ob.words_of(out.worker_msgs)
         _cmp_words(f"{what} packed_w", _u64(b["packed_w"][:, wlo:whi]).ravel(), ref_w.ravel(), rep)
         _cmp_words(f"{what} packed_s", _u64(b["packed_s"][wlo:whi]), out.server_msg.words, rep)
@@ -135,9 +154,10 @@ class Run:
 
 def parity_run(wl: Workload, steps: int, tensors: Optional[Sequence[int]] = None,
                grads_fn=None, split: bool = False, device="cuda",
-               state: Optional[Dict[str, torch.Tensor]] = None) -> Report:
+               state: Optional[Dict[str, torch.Tensor]] = None, residual: bool = False) -> Report:
     """Run `steps` steps on the device and on the oracle for `tensors` (all by
-    default), comparing after every step.  grads_fn(step) -> [W][N] device tensor."""
+    default), comparing after every step.  grads_fn(step) -> [W][N] device tensor.
+    residual=True runs the residual-form step and compares its materialized state."""
     from synth import grads_for_step
     tensors = list(range(wl.num_tensors)) if tensors is None else list(tensors)
     run = Run(wl, device, state)
@@ -152,11 +172,16 @@ def parity_run(wl: Workload, steps: int, tensors: Optional[Sequence[int]] = None
         else:
             g = grads_fn(k)
         host_g = [host_slice(g, run.off[t], run.off[t] + wl.numel[t]) for t in tensors]
-        (run.step_split if split else run.step)(g)
+        view = None
+        if residual:
+            run.step_residual(g, first=(k == 0))
+            view = run.materialized()
+        else:
+            (run.step_split if split else run.step)(g)
         torch.cuda.synchronize()
         for i, t in enumerate(tensors):
             out = ob.compression_step(ref[i], host_g[i], wl.beta1, wl.lr, wl.eps)
-            run.compare(t, out, rep, f"{wl.name} step {k} tensor {t}")
+            run.compare(t, out, rep, f"{wl.name} step {k} tensor {t}", state=view)
             ref[i] = out.state
         log(f"  {wl.name} step {k}: ok ({time.time() - t0:.1f}s, {len(tensors)} tensors)")
     run.ctx.close()
