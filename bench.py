@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "compressed optimizer-step elements/s and HBM GB/s (% of peak), 1 MI355X"
+KERNELS_SRC = os.path.join(ROOT, "error_compensated_bit_02_amd", "csrc", "kernels.hip")
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
 
 
@@ -59,6 +60,23 @@ def kernel_bytes_per_element(wl) -> dict:
         "server_residual": W / 8.0 + 8.0 + 1 / 8.0,           # read signs, z_prev; write z, server signs
         "update_residual": 1 / 8.0 + 12.0,                    # read server signs, v, p; write p
     }
+
+
+def counter_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
+    reading), or None when there is none or the kernels changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    with open(KERNELS_SRC, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != data.get("kernels_hip_sha256"):
+            return None
+    per = data.get("per_launch_bytes", {}).get(kernel)
+    return None if per is None else float(per)
 
 
 def cpu_baseline(wl, state, grads, sample_tensors: int) -> dict:
@@ -130,7 +148,7 @@ def time_form(form, wl, ctx, grads, steps, warmup, stream):
     return dt, kernels, st
 
 
-def summarize(wl, n_elem, steps, dt, kernels):
+def summarize(wl, n_elem, steps, dt, kernels, workload):
     ms_step = dt * 1e3 / steps
     b_alg = step_bytes_per_element(wl)
     step_gbps = b_alg * n_elem / (ms_step * 1e-3) / 1e9
@@ -139,8 +157,11 @@ def summarize(wl, n_elem, steps, dt, kernels):
     dom = max((k for k in kb if per_kernel[k]["launches"]), key=lambda k: per_kernel[k]["avg_ms"])
     dom_ms = per_kernel[dom]["avg_ms"]
     achieved = kb[dom] * n_elem / (dom_ms * 1e-3) / 1e9
+    traffic = counter_traffic(workload, dom)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "algorithmic_bytes": round(kb[dom] * n_elem),
                 "bytes_per_element": kb[dom], "avg_ms": round(dom_ms, 4)}
     return {
         "ms_per_step": ms_step,
@@ -208,7 +229,7 @@ def main() -> int:
         last_state = None
         torch.cuda.empty_cache()
         dt, kernels, last_state = time_form(form, wl, ctx, grads, args.steps, args.warmup, stream)
-        results[form] = summarize(wl, n_elem, args.steps, dt, kernels)
+        results[form] = summarize(wl, n_elem, args.steps, dt, kernels, wl.name)
         log(f"bench: {form}: {results[form]['ms_per_step']:.3f} ms/step, "
             f"{100 * results[form]['step_frac_of_peak']:.1f}% of peak")
 

@@ -35,6 +35,8 @@ SIGNATURES = {
     "ob_step": (ctypes.c_int, [_c_void_p] * 11 + [_f64, _c_void_p]),
     "ob_step_residual": (ctypes.c_int, [_c_void_p, _i32] + [_c_void_p] * 10 + [_f64, _c_void_p]),
     "ob_materialize": (ctypes.c_int, [_c_void_p] * 9),
+    "ob_warmup_step": (ctypes.c_int, [_c_void_p] * 5 + [_f64, _f64, _c_void_p]),
+    "ob_begin_compression": (ctypes.c_int, [_c_void_p] * 4),
     "ob_profile_enable": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_profile_kinds": (_i32, []),
     "ob_profile_kind_name": (ctypes.c_char_p, [_i32]),
@@ -218,6 +220,22 @@ class OneBitAdam:
             _ptr(err_w, f32, self.W * self.N, "err_w"), _ptr(err_s, f32, self.N, "err_s"),
             _ptr(m, f32, self.N, "m"), _stream(stream))
         _check(st, "ob_materialize")
+
+    def warmup_step(self, grads, m, v, params, beta2, lr, stream=None) -> None:
+        """One uncompressed Adam step on the workers' average gradient."""
+        f32 = (torch.float32,)
+        st = self.lib.ob_warmup_step(
+            self._ctx, self._grad_ptr(grads), _ptr(m, f32, self.N, "m"), _ptr(v, f32, self.N, "v"),
+            _ptr(params, f32, self.N, "params"), float(beta2), float(lr), _stream(stream))
+        _check(st, "ob_warmup_step")
+
+    def begin_compression(self, err_w, err_s, stream=None) -> None:
+        """Zero the error buffers at the switch from warmup to compression."""
+        f32 = (torch.float32,)
+        st = self.lib.ob_begin_compression(
+            self._ctx, _ptr(err_w, f32, self.W * self.N, "err_w"), _ptr(err_s, f32, self.N, "err_s"),
+            _stream(stream))
+        _check(st, "ob_begin_compression")
 
     # -- kernel timing -------------------------------------------------------
     def profile(self, enable: bool) -> None:

@@ -44,7 +44,7 @@ namespace {
 const char *const kKindNames[ob::K_NUM_KINDS] = {
     "worker_pass1", "scale_finalize", "worker_pass2", "server_pass1",
     "server_pass2", "server_pass2_update", "apply_update", "worker_residual",
-    "server_residual", "update_residual", "materialize"};
+    "server_residual", "update_residual", "materialize", "warmup", "zero_errors"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -370,6 +370,26 @@ int ob_materialize(ob_ctx *c, const float *x_w, const float *scale_w, const floa
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ob::MaterializeArgs a{x_w, scale_w, z, scale_s, err_w, err_s, m};
   return timed(c, ob::K_MATERIALIZE, s, [&] { ob::launch_materialize(c->geo, a, s); });
+}
+
+int ob_warmup_step(ob_ctx *c, const void *grads, float *m, float *v, float *params, double beta2,
+                   double lr, void *stream) {
+  if (c == nullptr || !std::isfinite(lr)) return OB_ERR_INVALID;
+  if (!std::isfinite(beta2) || beta2 < 0.0 || beta2 >= 1.0) return OB_ERR_INVALID;
+  const int st = check_ptrs(grads, m, v, params);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ob::WarmupArgs a{grads, m, v, params, c->c1, c->c2, static_cast<float>(beta2),
+                         static_cast<float>(1.0 - beta2), static_cast<float>(lr), c->eps};
+  return timed(c, ob::K_WARMUP, s, [&] { ob::launch_warmup(c->geo, c->bf16, a, s); });
+}
+
+int ob_begin_compression(ob_ctx *c, float *err_w, float *err_s, void *stream) {
+  if (c == nullptr) return OB_ERR_INVALID;
+  const int st = check_ptrs(err_w, err_s);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, ob::K_ZERO_ERRORS, s, [&] { ob::launch_zero_errors(c->geo, err_w, err_s, s); });
 }
 
 int ob_profile_enable(ob_ctx *c, int32_t enable) {

@@ -60,6 +60,8 @@ enum Kind {
   K_SERVER_RESIDUAL,
   K_UPDATE_RESIDUAL,
   K_MATERIALIZE,
+  K_WARMUP,
+  K_ZERO_ERRORS,
   K_NUM_KINDS
 };
 
@@ -111,11 +113,21 @@ struct MaterializeArgs {     // inputs and outputs may alias
   float *m;
 };
 
+struct WarmupArgs {
+  const void *grads;         // [W][N] fp32 or bf16
+  float *m;                  // [N]
+  float *v;                  // [N]
+  float *params;             // [N]
+  float c1, c2, b2, cb2, lr, eps;
+};
+
 void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s);
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0, int nrows,
                            float *out, hipStream_t s);
 void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s);
 void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStream_t s);
 void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s);
+void launch_warmup(const Geometry &g, bool bf16, const WarmupArgs &a, hipStream_t s);
+void launch_zero_errors(const Geometry &g, float *err_w, float *err_s, hipStream_t s);
 
 }  // namespace ob

@@ -472,6 +472,76 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(Geometry g, Materia
     materialize_tile<false>(tl, g, a);
 }
 
+// ---------------------------------------------------------------------------
+// warmup phase: uncompressed Adam on the workers' average gradient
+//   gbar = (ascending sum over w of g_w) / W
+//   m = c1*m + c2*gbar;  v = b2*v + cb2*(gbar*gbar);  p -= lr * (m / (sqrt(v) + eps))
+// ---------------------------------------------------------------------------
+template <typename G, bool kFull, bool kPow2>
+__device__ __forceinline__ void warmup_tile(const Tile &tl, const Geometry &g, const WarmupArgs &a) {
+  const Lanes ln = lanes_of<kFull>(tl);
+  const G *grads = static_cast<const G *>(a.grads) + ln.base + ln.lane;
+  const float wf = static_cast<float>(g.W);
+  const float inv_w = 1.0f / wf;   // exact when W is a power of two
+  // eight elements per lane at a time keep the W-long sums in registers
+  constexpr int kChunk = 8;
+#pragma unroll
+  for (int c0 = 0; c0 < kPerLane; c0 += kChunk) {
+    float acc[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) acc[j] = 0.0f;
+    for (int w = 0; w < g.W; ++w) {
+      const G *gw = grads + static_cast<size_t>(w) * g.N;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (in_tile<kFull>(tl, ln, c0 + j)) acc[j] = acc[j] + grad_value(gw + 64 * (c0 + j));
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (!in_tile<kFull>(tl, ln, c0 + j)) continue;
+      const int64_t i = ln.base + 64 * (c0 + j) + ln.lane;
+      const float gbar = kPow2 ? acc[j] * inv_w : acc[j] / wf;
+      const float m = a.c1 * a.m[i] + a.c2 * gbar;
+      const float v = a.b2 * a.v[i] + a.cb2 * (gbar * gbar);
+      const float d = __builtin_sqrtf(v) + a.eps;
+      const float u = m / d;
+      a.m[i] = m;
+      a.v[i] = v;
+      a.params[i] = a.params[i] - a.lr * u;
+    }
+  }
+}
+
+template <typename G, bool kPow2>
+__global__ __launch_bounds__(kBlock) void warmup_kernel(Geometry g, WarmupArgs a) {
+  const Tile tl = g.tiles[blockIdx.x];
+  if (tl.len == kTile)
+    warmup_tile<G, true, kPow2>(tl, g, a);
+  else
+    warmup_tile<G, false, kPow2>(tl, g, a);
+}
+
+// Zero the worker and server errors (tensor ranges only; padding untouched).
+template <bool kFull>
+__device__ __forceinline__ void zero_errors_tile(const Tile &tl, const Geometry &g, float *err_w,
+                                                 float *err_s) {
+  const Lanes ln = lanes_of<kFull>(tl);
+  for (int w = 0; w <= g.W; ++w) {
+    float *row = (w < g.W ? err_w + static_cast<size_t>(w) * g.N : err_s) + ln.base + ln.lane;
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c)
+      if (in_tile<kFull>(tl, ln, c)) row[64 * c] = 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void zero_errors_kernel(Geometry g, float *err_w, float *err_s) {
+  const Tile tl = g.tiles[blockIdx.x];
+  if (tl.len == kTile)
+    zero_errors_tile<true>(tl, g, err_w, err_s);
+  else
+    zero_errors_tile<false>(tl, g, err_w, err_s);
+}
+
 template <typename G>
 void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStream_t s) {
   const dim3 grid(g.num_tiles), block(kBlock);
@@ -539,6 +609,22 @@ void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStre
 
 void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(materialize_kernel, dim3(g.num_tiles), dim3(kBlock), 0, s, g, a);
+}
+
+void launch_warmup(const Geometry &g, bool bf16, const WarmupArgs &a, hipStream_t s) {
+  const dim3 grid(g.num_tiles), block(kBlock);
+  const bool pow2 = (g.W & (g.W - 1)) == 0;
+  if (bf16) {
+    if (pow2) hipLaunchKernelGGL((warmup_kernel<uint16_t, true>), grid, block, 0, s, g, a);
+    else hipLaunchKernelGGL((warmup_kernel<uint16_t, false>), grid, block, 0, s, g, a);
+  } else {
+    if (pow2) hipLaunchKernelGGL((warmup_kernel<float, true>), grid, block, 0, s, g, a);
+    else hipLaunchKernelGGL((warmup_kernel<float, false>), grid, block, 0, s, g, a);
+  }
+}
+
+void launch_zero_errors(const Geometry &g, float *err_w, float *err_s, hipStream_t s) {
+  hipLaunchKernelGGL(zero_errors_kernel, dim3(g.num_tiles), dim3(kBlock), 0, s, g, err_w, err_s);
 }
 
 }  // namespace ob

@@ -161,6 +161,25 @@ int ob_step_residual(ob_ctx *ctx, int32_t first, const void *grads, const float 
 int ob_materialize(ob_ctx *ctx, const float *x_w, const float *scale_w, const float *z,
                    const float *scale_s, float *err_w, float *err_s, float *m, void *stream);
 
+/* Warmup phase: one uncompressed Adam step on the workers' average gradient,
+ * the first phase of the method (the review of "1-bit Adam ...", Proposed
+ * method, bullet 1: full-precision Adam for about the first 20% of steps,
+ * whose variance the compression phase then keeps fixed, bullet 2):
+ *   gbar = (sum over w = 0..W-1, ascending, from +0, of g_w[i]) / W
+ *   m[i] = c1*m[i] + c2*gbar
+ *   v[i] = fp32(beta2)*v[i] + fp32(1 - beta2)*(gbar*gbar)
+ *   p[i] = p[i] - lr * (m[i] / (sqrt(v[i]) + eps))      (no bias correction)
+ * grads [W][N] read; m, v, params [N] read and overwritten.  beta2 in [0, 1),
+ * lr finite. */
+int ob_warmup_step(ob_ctx *ctx, const void *grads, float *m, float *v, float *params,
+                   double beta2, double lr, void *stream);
+
+/* The switch from warmup to compression: v is kept as it is from now on
+ * (frozen) and the error buffers start from zero.  Writes 0 to every tensor
+ * element of err_w [W][N] and err_s [N] (padding untouched).  The next step
+ * is ob_step, or ob_step_residual with first != 0. */
+int ob_begin_compression(ob_ctx *ctx, float *err_w, float *err_s, void *stream);
+
 /* Kernel timing for measurement.  With profiling on, every kernel the context
  * launches is bracketed by HIP events on its stream.  ob_profile_read waits for
  * the recorded events, writes per kernel kind the summed milliseconds and the
