@@ -102,6 +102,7 @@ ob::WorkerArgs worker_args(ob_ctx *c, int w0, int w1, const void *grads, const f
   a.partials = c->partials;
   a.w0 = w0;
   a.w1 = w1;
+  a.wgroup = ob::worker_group_size(w1 - w0, c->num_tiles);
   a.c1 = c->c1;
   a.c2 = c->c2;
   return a;

@@ -18,6 +18,9 @@ namespace ob {
 #ifndef OB_TILE
 #define OB_TILE 8192
 #endif
+#ifndef OB_MAX_GROUP
+#define OB_MAX_GROUP 16
+#endif
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 constexpr int kTile = OB_TILE;
@@ -77,9 +80,23 @@ struct WorkerArgs {
   const uint64_t *packed_s;  // [Nw] previous server message (residual)
   const float *scale_s;      // [T]  previous server scales (residual)
   double2 *partials;
-  int w0, w1;
+  int w0, w1;                // workers [w0, w1)
+  int wgroup;                // workers per workgroup (see worker_group_size)
   float c1, c2;
 };
+
+// Workers handled by one workgroup of a worker pass.  At most kMaxGroup, so
+// the workgroups resident at once stream few rows; fewer when the tile count
+// alone would leave the launch short of kMinBlocks workgroups (many small
+// launches of a small list would leave most of the 256 CUs idle at the tail).
+constexpr int kMaxGroup = OB_MAX_GROUP;
+constexpr int kMinBlocks = 8192;
+inline int worker_group_size(int workers, int num_tiles) {
+  int groups = (workers + kMaxGroup - 1) / kMaxGroup;
+  const int want = (kMinBlocks + num_tiles - 1) / num_tiles;
+  if (groups < want) groups = want < workers ? want : workers;
+  return (workers + groups - 1) / groups;
+}
 
 struct ServerArgs {
   const uint64_t *packed_w;  // [W][Nw]

@@ -96,6 +96,7 @@ struct PartialSink {
   double2 (*red)[kWaves];
   double2 *partials;   // row-major [rows][num_tiles]
   int num_tiles;
+  int tile;            // column of this workgroup's tile
 };
 
 __device__ __forceinline__ void park_partial(const PartialSink &ps, int slot, int wave, double hi,
@@ -112,7 +113,7 @@ __device__ __forceinline__ void flush_partials(const PartialSink &ps, int row0, 
     double h = ps.red[r][0].x, l = ps.red[r][0].y;
 #pragma unroll
     for (int v = 1; v < kWaves; ++v) dd_add(h, l, ps.red[r][v].x, ps.red[r][v].y);
-    ps.partials[static_cast<size_t>(row0 + r) * ps.num_tiles + blockIdx.x] = make_double2(h, l);
+    ps.partials[static_cast<size_t>(row0 + r) * ps.num_tiles + ps.tile] = make_double2(h, l);
   }
   __syncthreads();
 }
@@ -157,11 +158,13 @@ __device__ __forceinline__ uint64_t load_words(const uint64_t *row, const Lanes 
 }
 
 // +-s for this lane's element 64 c + lane, from the words held by load_words.
-__device__ __forceinline__ float signed_scale(uint64_t words, int c, int lane, float s) {
+// Word c, broadcast to scalar registers, is a lane mask (bit l <-> lane l), so
+// the choice between s and -s is one v_cndmask with the word as its mask.
+__device__ __forceinline__ float signed_scale(uint64_t words, int c, float s) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(words)), c);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(words >> 32)), c);
-  const uint32_t half = lane < 32 ? lo : hi;
-  return ((half >> (lane & 31)) & 1u) ? s : -s;
+  const uint64_t word = (static_cast<uint64_t>(hi) << 32) | lo;
+  return __builtin_amdgcn_inverse_ballot_w64(word) ? s : -s;
 }
 
 // ---------------------------------------------------------------------------
@@ -176,7 +179,7 @@ enum { kPass1 = 0, kPass2 = 1, kResidFirst = 2, kResid = 3 };
 
 template <int kMode, typename G, bool kFull>
 __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, const WorkerArgs &a,
-                                            const PartialSink &sink) {
+                                            int w_lo, int w_hi, const PartialSink &sink) {
   const Lanes ln = lanes_of<kFull>(tl);
   const int t = tl.tensor;
   float mr[kPerLane];
@@ -185,7 +188,7 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
     const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c)
-      mr[c] = in_tile<kFull>(tl, ln, c) ? signed_scale(words, c, ln.lane, ss) : 0.0f;
+      mr[c] = in_tile<kFull>(tl, ln, c) ? signed_scale(words, c, ss) : 0.0f;
   } else {
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c)
@@ -204,7 +207,7 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
       edst[c] = ok ? ew[64 * c] : 0.0f;
     }
   };
-  for (int w = a.w0; w < a.w1; ++w) {
+  for (int w = w_lo; w < w_hi; ++w) {
     float *ew = a.err_w + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
     // kPass2: this step's scale; kResid: the previous step's scale
     const float s = (kMode == kPass2 || kMode == kResid) ? a.scale_w[static_cast<size_t>(w) * g.T + t] : 0.0f;
@@ -233,21 +236,28 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
     }
     if (ln.lane < ln.nwords)
       a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane] = word;
-    const int slot = (w - a.w0) % kFlushRows;
+    const int slot = (w - w_lo) % kFlushRows;
     park_partial(sink, slot, ln.wave, hi, lo);
-    if (slot == kFlushRows - 1 || w == a.w1 - 1) flush_partials(sink, w - slot, slot + 1);
+    if (slot == kFlushRows - 1 || w == w_hi - 1) flush_partials(sink, w - slot, slot + 1);
   }
 }
 
+// Workgroup b handles tile b % num_tiles for the worker group b / num_tiles
+// (workers [w0 + grp*wgroup, ...)): group-major, so the workgroups resident at
+// one time stream a few workers' rows through contiguous memory.
 template <typename G, int kMode>
 __global__ __launch_bounds__(kBlock) void worker_kernel(Geometry g, WorkerArgs a) {
   __shared__ double2 red[kFlushRows][kWaves];
-  const PartialSink sink{red, a.partials, g.num_tiles};
-  const Tile tl = g.tiles[blockIdx.x];
+  const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(g.num_tiles));
+  const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(g.num_tiles));
+  const int w_lo = a.w0 + grp * a.wgroup;
+  const int w_hi = min(a.w1, w_lo + a.wgroup);
+  const PartialSink sink{red, a.partials, g.num_tiles, tile};
+  const Tile tl = g.tiles[tile];
   if (tl.len == kTile)
-    worker_tile<kMode, G, true>(tl, g, a, sink);
+    worker_tile<kMode, G, true>(tl, g, a, w_lo, w_hi, sink);
   else
-    worker_tile<kMode, G, false>(tl, g, a, sink);
+    worker_tile<kMode, G, false>(tl, g, a, w_lo, w_hi, sink);
 }
 
 // ---------------------------------------------------------------------------
@@ -317,7 +327,7 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, c
     for (int j = 0; j < kGroup; ++j) {
       if (w0 + j >= g.W) break;
 #pragma unroll
-      for (int c = 0; c < kPerLane; ++c) acc[c] = acc[c] + signed_scale(words[j], c, ln.lane, sw[j]);
+      for (int c = 0; c < kPerLane; ++c) acc[c] = acc[c] + signed_scale(words[j], c, sw[j]);
     }
   }
   const float wf = static_cast<float>(g.W);
@@ -391,7 +401,7 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, c
 template <int kMode, bool kPow2>
 __global__ __launch_bounds__(kBlock) void server_kernel(Geometry g, ServerArgs a) {
   __shared__ double2 red[1][kWaves];
-  const PartialSink sink{red, a.partials, g.num_tiles};
+  const PartialSink sink{red, a.partials, g.num_tiles, static_cast<int>(blockIdx.x)};
   const Tile tl = g.tiles[blockIdx.x];
   if (tl.len == kTile)
     server_tile<kMode, true, kPow2>(tl, g, a, sink);
@@ -417,7 +427,7 @@ __device__ __forceinline__ void update_tile(const Tile &tl, const UpdateArgs &a)
   }
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
-    const float mv = signed_scale(words, c, ln.lane, ss);  // every lane takes part in the broadcast
+    const float mv = signed_scale(words, c, ss);  // every lane takes part in the broadcast
     if (!in_tile<kFull>(tl, ln, c)) continue;
     const int64_t i = ln.base + 64 * c + ln.lane;
     const float d = __builtin_sqrtf(vv[c]) + a.eps;
@@ -544,7 +554,8 @@ __global__ __launch_bounds__(kBlock) void zero_errors_kernel(Geometry g, float *
 
 template <typename G>
 void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStream_t s) {
-  const dim3 grid(g.num_tiles), block(kBlock);
+  const int groups = (a.w1 - a.w0 + a.wgroup - 1) / a.wgroup;
+  const dim3 grid(static_cast<unsigned>(g.num_tiles) * static_cast<unsigned>(groups)), block(kBlock);
   switch (mode) {
     case kPass1: hipLaunchKernelGGL((worker_kernel<G, kPass1>), grid, block, 0, s, g, a); break;
     case kPass2: hipLaunchKernelGGL((worker_kernel<G, kPass2>), grid, block, 0, s, g, a); break;
