@@ -184,6 +184,8 @@ def main() -> int:
                     help="state form between steps; both forms give bit-identical trajectories. "
                          "'both' times the residual form (the headline) and the strict form")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct gradient sets cycled")
+    ap.add_argument("--server-chunks", type=int, default=1,
+                    help="partitioned server: one server scale per tensor chunk (1 = per tensor)")
     ap.add_argument("--cpu-sample-tensors", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -218,6 +220,8 @@ def main() -> int:
     log(f"bench: {wl.name}: {wl.num_tensors} tensors, {n_elem} elements, W={wl.workers}, "
         f"grads {wl.grad_dtype}; steps={args.steps} warmup={args.warmup}")
     ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
+    if args.server_chunks != 1:
+        ctx.set_server_chunks(args.server_chunks)
     sets = max(1, min(args.grad_sets, args.steps + args.warmup))
     grads = [grads_for_step(wl, k, "cuda") for k in range(sets)]
     torch.cuda.synchronize()
@@ -241,7 +245,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "tensors": wl.num_tensors, "elements": n_elem,
                    "workers": wl.workers, "grad_dtype": wl.grad_dtype,
-                   "grad_sets": sets, "state_form": forms[0]},
+                   "grad_sets": sets, "state_form": forms[0], "server_chunks": args.server_chunks},
         "step_hbm_gbps_algorithmic": head["step_hbm_gbps_algorithmic"],
         "step_frac_of_peak": head["step_frac_of_peak"],
         "step_bytes_per_element": step_bytes_per_element(wl),

@@ -37,6 +37,8 @@ SIGNATURES = {
     "ob_materialize": (ctypes.c_int, [_c_void_p] * 9),
     "ob_warmup_step": (ctypes.c_int, [_c_void_p] * 5 + [_f64, _f64, _c_void_p]),
     "ob_begin_compression": (ctypes.c_int, [_c_void_p] * 4),
+    "ob_set_server_chunks": (ctypes.c_int, [_c_void_p, _i32]),
+    "ob_server_scale_count": (_i32, [_c_void_p]),
     "ob_profile_enable": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_profile_kinds": (_i32, []),
     "ob_profile_kind_name": (ctypes.c_char_p, [_i32]),
@@ -126,6 +128,12 @@ class OneBitAdam:
         _check(self.lib.ob_init(ctypes.byref(ctx), self.T, arr, self.W, code, self.beta1, self.eps),
                "ob_init")
         self._ctx = ctx
+        self.S = self.lib.ob_server_scale_count(self._ctx)
+
+    def set_server_chunks(self, chunks: int) -> None:
+        """Partition the server C ways (one scale per tensor chunk); see include/ob.h."""
+        _check(self.lib.ob_set_server_chunks(self._ctx, int(chunks)), "ob_set_server_chunks")
+        self.S = self.lib.ob_server_scale_count(self._ctx)
 
     def close(self) -> None:
         if getattr(self, "_ctx", None):
@@ -146,7 +154,7 @@ class OneBitAdam:
             "packed_w": torch.zeros(self.W, self.Nw, dtype=torch.int64, device=d),
             "scale_w": torch.zeros(self.W, self.T, dtype=torch.float32, device=d),
             "packed_s": torch.zeros(self.Nw, dtype=torch.int64, device=d),
-            "scale_s": torch.zeros(self.T, dtype=torch.float32, device=d),
+            "scale_s": torch.zeros(self.S, dtype=torch.float32, device=d),
         }
 
     def _grad_ptr(self, grads: torch.Tensor) -> int:
@@ -171,14 +179,14 @@ class OneBitAdam:
             self._ctx, _ptr(packed_w, (torch.int64,), self.W * self.Nw, "packed_w"),
             _ptr(scale_w, f32, self.W * self.T, "scale_w"), _ptr(err_s, f32, self.N, "err_s"),
             _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
-            _ptr(scale_s, f32, self.T, "scale_s"), _stream(stream))
+            _ptr(scale_s, f32, self.S, "scale_s"), _stream(stream))
         _check(st, "ob_server_reduce")
 
     def apply_update(self, packed_s, scale_s, v, m, params, lr, stream=None) -> None:
         f32 = (torch.float32,)
         st = self.lib.ob_apply_update(
             self._ctx, _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
-            _ptr(scale_s, f32, self.T, "scale_s"), _ptr(v, f32, self.N, "v"),
+            _ptr(scale_s, f32, self.S, "scale_s"), _ptr(v, f32, self.N, "v"),
             _ptr(m, f32, self.N, "m"), _ptr(params, f32, self.N, "params"), float(lr),
             _stream(stream))
         _check(st, "ob_apply_update")
@@ -193,7 +201,7 @@ class OneBitAdam:
             _ptr(packed_w, (torch.int64,), self.W * self.Nw, "packed_w"),
             _ptr(scale_w, f32, self.W * self.T, "scale_w"),
             _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
-            _ptr(scale_s, f32, self.T, "scale_s"), float(lr), _stream(stream))
+            _ptr(scale_s, f32, self.S, "scale_s"), float(lr), _stream(stream))
         _check(st, "ob_step")
 
     def step_residual(self, first, grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s,
@@ -208,7 +216,7 @@ class OneBitAdam:
             _ptr(packed_w, (torch.int64,), self.W * self.Nw, "packed_w"),
             _ptr(scale_w, f32, self.W * self.T, "scale_w"),
             _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
-            _ptr(scale_s, f32, self.T, "scale_s"), float(lr), _stream(stream))
+            _ptr(scale_s, f32, self.S, "scale_s"), float(lr), _stream(stream))
         _check(st, "ob_step_residual")
 
     def materialize(self, x_w, scale_w, z, scale_s, err_w, err_s, m, stream=None) -> None:
@@ -216,7 +224,7 @@ class OneBitAdam:
         f32 = (torch.float32,)
         st = self.lib.ob_materialize(
             self._ctx, _ptr(x_w, f32, self.W * self.N, "x_w"), _ptr(scale_w, f32, self.W * self.T, "scale_w"),
-            _ptr(z, f32, self.N, "z"), _ptr(scale_s, f32, self.T, "scale_s"),
+            _ptr(z, f32, self.N, "z"), _ptr(scale_s, f32, self.S, "scale_s"),
             _ptr(err_w, f32, self.W * self.N, "err_w"), _ptr(err_s, f32, self.N, "err_s"),
             _ptr(m, f32, self.N, "m"), _stream(stream))
         _check(st, "ob_materialize")

@@ -3,6 +3,7 @@
 // optional per-kernel event timing.
 #include "ob.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -31,6 +32,12 @@ struct ob_ctx {
   std::vector<int64_t> off;
   int64_t N = 0;
   int32_t num_tiles = 0;
+  std::vector<int32_t> tile_begin;   // host copy [T+1]
+  int32_t server_chunks = 1;
+  int32_t S = 0;                     // server scales (pieces)
+  int32_t *d_tile_piece = nullptr;   // device views into scratch
+  int32_t *d_piece_begin = nullptr;
+  int64_t *d_piece_numel = nullptr;
   void *scratch = nullptr;         // one device allocation: tiles | tile_begin | numel | partials
   ob::Geometry geo{};
   double2 *partials = nullptr;     // (W+1) x num_tiles
@@ -130,7 +137,7 @@ int do_compress(ob_ctx *c, int w0, int w1, const void *grads, const float *m, fl
   });
   if (st) return st;
   st = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    ob::launch_scale_finalize(g, c->partials, w0, w1 - w0,
+    ob::launch_scale_finalize(g, c->partials, w0, w1 - w0, g.tile_begin, g.numel, c->T,
                               scale_w + static_cast<size_t>(w0) * c->T, s);
   });
   if (st) return st;
@@ -148,8 +155,43 @@ int do_server_first(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, f
   });
   if (st) return st;
   return timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    ob::launch_scale_finalize(g, c->partials, c->W, 1, scale_s, s);
+    ob::launch_scale_finalize(g, c->partials, c->W, 1, g.piece_begin, g.piece_numel, c->S,
+                              scale_s, s);
   });
+}
+
+// Server pieces for a C-way partitioned server: chunk j of tensor t is a run
+// of q_t = ceil(k_t / C) of its k_t tiles (whole 8192-element tiles, the last
+// run shorter), so tensor t has ceil(k_t / q_t) <= C pieces.  C = 1 gives one
+// piece per tensor.  Uploads the three tables (synchronous copies).
+int upload_pieces(ob_ctx *c, int32_t chunks) {
+  std::vector<int32_t> tile_piece(c->num_tiles), piece_begin;
+  std::vector<int64_t> piece_numel;
+  for (int32_t t = 0; t < c->T; ++t) {
+    const int32_t k = c->tile_begin[t + 1] - c->tile_begin[t];
+    const int32_t q = (k + chunks - 1) / chunks;
+    for (int32_t i = 0; i < k; i += q) {
+      const int32_t piece = static_cast<int32_t>(piece_begin.size());
+      piece_begin.push_back(c->tile_begin[t] + i);
+      const int64_t lo = static_cast<int64_t>(i) * ob::kTile;
+      const int64_t hi = std::min<int64_t>(static_cast<int64_t>(i + q) * ob::kTile, c->numel[t]);
+      piece_numel.push_back(hi - lo);
+      for (int32_t j = i; j < std::min(i + q, k); ++j) tile_piece[c->tile_begin[t] + j] = piece;
+    }
+  }
+  piece_begin.push_back(c->num_tiles);
+  const size_t S = piece_numel.size();
+  if (hipMemcpy(c->d_tile_piece, tile_piece.data(), tile_piece.size() * sizeof(int32_t),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(c->d_piece_begin, piece_begin.data(), piece_begin.size() * sizeof(int32_t),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(c->d_piece_numel, piece_numel.data(), S * sizeof(int64_t),
+                hipMemcpyHostToDevice) != hipSuccess)
+    return OB_ERR_DEVICE;
+  c->server_chunks = chunks;
+  c->S = static_cast<int32_t>(S);
+  c->geo.S = c->S;
+  return OB_OK;
 }
 
 }  // namespace
@@ -220,12 +262,18 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   }
   tile_begin[num_tensors] = static_cast<int32_t>(tiles.size());
   c->num_tiles = static_cast<int32_t>(tiles.size());
+  c->tile_begin = tile_begin;
 
   // one allocation, 256-byte aligned sections
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t b_tiles = up(tiles.size() * sizeof(ob::Tile));
   const size_t b_begin = up(tile_begin.size() * sizeof(int32_t));
   const size_t b_numel = up(c->numel.size() * sizeof(int64_t));
+  // server-piece tables, sized for the most pieces (one per tile)
+  const size_t b_tpiece = up(tiles.size() * sizeof(int32_t));
+  const size_t b_pbegin = up((tiles.size() + 1) * sizeof(int32_t));
+  const size_t b_pnumel = up(tiles.size() * sizeof(int64_t));
+  const size_t b_pieces = b_tpiece + b_pbegin + b_pnumel;
   const size_t b_part =
       up(ob::partials_count(num_workers, static_cast<int>(tiles.size())) * sizeof(double2));
   std::vector<unsigned char> host(b_tiles + b_begin + b_numel, 0);
@@ -237,7 +285,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   std::copy(reinterpret_cast<const unsigned char *>(c->numel.data()),
             reinterpret_cast<const unsigned char *>(c->numel.data() + c->numel.size()),
             host.data() + b_tiles + b_begin);
-  if (hipMalloc(&c->scratch, host.size() + b_part) != hipSuccess) {
+  if (hipMalloc(&c->scratch, host.size() + b_pieces + b_part) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return OB_ERR_NOMEM;
@@ -251,12 +299,25 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->geo.tiles = reinterpret_cast<const ob::Tile *>(base);
   c->geo.tile_begin = reinterpret_cast<const int32_t *>(base + b_tiles);
   c->geo.numel = reinterpret_cast<const int64_t *>(base + b_tiles + b_begin);
-  c->partials = reinterpret_cast<double2 *>(base + b_tiles + b_begin + b_numel);
+  unsigned char *pieces = base + b_tiles + b_begin + b_numel;
+  c->d_tile_piece = reinterpret_cast<int32_t *>(pieces);
+  c->d_piece_begin = reinterpret_cast<int32_t *>(pieces + b_tpiece);
+  c->d_piece_numel = reinterpret_cast<int64_t *>(pieces + b_tpiece + b_pbegin);
+  c->geo.tile_piece = c->d_tile_piece;
+  c->geo.piece_begin = c->d_piece_begin;
+  c->geo.piece_numel = c->d_piece_numel;
+  c->partials = reinterpret_cast<double2 *>(pieces + b_pieces);
   c->geo.num_tiles = c->num_tiles;
   c->geo.T = c->T;
   c->geo.W = c->W;
   c->geo.N = c->N;
   c->geo.Nw = c->N / 64;
+  const int pr = upload_pieces(c, 1);
+  if (pr != OB_OK) {
+    (void)hipFree(c->scratch);
+    delete c;
+    return pr;
+  }
   *out = c;
   return OB_OK;
 }
@@ -347,7 +408,7 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   });
   if (r) return r;
   r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    ob::launch_scale_finalize(g, c->partials, 0, c->W, scale_w, s);
+    ob::launch_scale_finalize(g, c->partials, 0, c->W, g.tile_begin, g.numel, c->T, scale_w, s);
   });
   if (r) return r;
   const ob::ServerArgs sa = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
@@ -356,7 +417,8 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   });
   if (r) return r;
   r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    ob::launch_scale_finalize(g, c->partials, c->W, 1, scale_s, s);
+    ob::launch_scale_finalize(g, c->partials, c->W, 1, g.piece_begin, g.piece_numel, c->S,
+                              scale_s, s);
   });
   if (r) return r;
   const ob::UpdateArgs ua{packed_s, scale_s, v, nullptr, params, static_cast<float>(lr), c->eps};
@@ -392,6 +454,14 @@ int ob_begin_compression(ob_ctx *c, float *err_w, float *err_s, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   return timed(c, ob::K_ZERO_ERRORS, s, [&] { ob::launch_zero_errors(c->geo, err_w, err_s, s); });
 }
+
+int ob_set_server_chunks(ob_ctx *c, int32_t chunks) {
+  if (c == nullptr || chunks < 1) return OB_ERR_INVALID;
+  if (hipDeviceSynchronize() != hipSuccess) return OB_ERR_DEVICE;   // tables may be in use
+  return upload_pieces(c, chunks);
+}
+
+int32_t ob_server_scale_count(const ob_ctx *c) { return c == nullptr ? -1 : c->S; }
 
 int ob_profile_enable(ob_ctx *c, int32_t enable) {
   if (c == nullptr) return OB_ERR_INVALID;

@@ -33,11 +33,17 @@ struct Tile {
   int32_t tensor;  // tensor the tile belongs to
 };
 
-// Device-side description of a tensor list.
+// Device-side description of a tensor list.  The server's scales are one per
+// "piece": a tensor, or with a C-way partitioned server one chunk of a tensor
+// (a run of whole tiles); with C = 1 the pieces are the tensors.
 struct Geometry {
   const Tile *tiles;
   const int32_t *tile_begin;  // [T+1]: tiles of tensor t are tile_begin[t] .. tile_begin[t+1]-1
   const int64_t *numel;       // [T]
+  const int32_t *tile_piece;  // [num_tiles]: server-scale index of each tile
+  const int32_t *piece_begin; // [S+1]: tiles of piece j are piece_begin[j] .. piece_begin[j+1]-1
+  const int64_t *piece_numel; // [S]
+  int32_t S;                  // number of server scales
   int32_t num_tiles;
   int32_t T;
   int32_t W;
@@ -139,8 +145,12 @@ struct WarmupArgs {
 };
 
 void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s);
+// Scales of rows [row0, row0 + nrows) of the partials over `count` items
+// whose tile ranges are begin[i] .. begin[i+1]-1 and sizes numel[i]; row r's
+// scale of item i goes to out[(r - row0) * count + i].
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0, int nrows,
-                           float *out, hipStream_t s);
+                           const int32_t *begin, const int64_t *numel, int count, float *out,
+                           hipStream_t s);
 void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s);
 void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStream_t s);
 void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s);

@@ -184,7 +184,7 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
   const int t = tl.tensor;
   float mr[kPerLane];
   if (kMode == kResid) {
-    const float ss = a.scale_s[t];
+    const float ss = a.scale_s[g.tile_piece[sink.tile]];
     const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c)
@@ -266,16 +266,18 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(Geometry g, WorkerArgs a
 __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
                                                          const double2 *__restrict__ partials,
                                                          int row0, int nrows,
-                                                         float *__restrict__ out) {
+                                                         const int32_t *__restrict__ begin,
+                                                         const int64_t *__restrict__ numel,
+                                                         int count, float *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t id = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (id >= static_cast<int64_t>(nrows) * g.T) return;  // whole wavefront leaves together
-  const int r = static_cast<int>(id / g.T);
-  const int t = static_cast<int>(id % g.T);
+  if (id >= static_cast<int64_t>(nrows) * count) return;  // whole wavefront leaves together
+  const int r = static_cast<int>(id / count);
+  const int item = static_cast<int>(id % count);
   const double2 *row = partials + static_cast<size_t>(row0 + r) * g.num_tiles;
   double hi = 0.0, lo = 0.0;
-  const int end = g.tile_begin[t + 1];
-  for (int i = g.tile_begin[t] + lane; i < end; i += 64) {
+  const int end = begin[item + 1];
+  for (int i = begin[item] + lane; i < end; i += 64) {
     const double2 p = row[i];
     dd_add(hi, lo, p.x, p.y);
   }
@@ -287,8 +289,8 @@ __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
   }
   if (lane == 0) {
     const double S = hi + lo;                          // fl64 of the sum of squares
-    const double q = S / static_cast<double>(g.numel[t]);
-    out[static_cast<size_t>(r) * g.T + t] = static_cast<float>(__builtin_sqrt(q));
+    const double q = S / static_cast<double>(numel[item]);
+    out[static_cast<size_t>(r) * count + item] = static_cast<float>(__builtin_sqrt(q));
   }
 }
 
@@ -334,7 +336,8 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, c
   const float inv_w = 1.0f / wf;   // exact when W is a power of two
   float *es = a.err_s + ln.base + ln.lane;
   // kS2/kS2Update: this step's server scale; kSResid: the previous step's
-  const float ss = (kMode == kS2 || kMode == kS2Update || kMode == kSResid) ? a.scale_s[t] : 0.0f;
+  const float ss = (kMode == kS2 || kMode == kS2Update || kMode == kSResid)
+                       ? a.scale_s[g.tile_piece[blockIdx.x]] : 0.0f;
   float z[kPerLane];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
@@ -414,9 +417,9 @@ __global__ __launch_bounds__(kBlock) void server_kernel(Geometry g, ServerArgs a
 // p <- p - lr * (m / (sqrt(v) + eps))
 // ---------------------------------------------------------------------------
 template <bool kStoreM, bool kFull>
-__device__ __forceinline__ void update_tile(const Tile &tl, const UpdateArgs &a) {
+__device__ __forceinline__ void update_tile(const Tile &tl, const Geometry &g, const UpdateArgs &a) {
   const Lanes ln = lanes_of<kFull>(tl);
-  const float ss = a.scale_s[tl.tensor];
+  const float ss = a.scale_s[g.tile_piece[blockIdx.x]];
   const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
   float vv[kPerLane], pv[kPerLane];
 #pragma unroll
@@ -441,9 +444,9 @@ template <bool kStoreM>
 __global__ __launch_bounds__(kBlock) void update_kernel(Geometry g, UpdateArgs a) {
   const Tile tl = g.tiles[blockIdx.x];
   if (tl.len == kTile)
-    update_tile<kStoreM, true>(tl, a);
+    update_tile<kStoreM, true>(tl, g, a);
   else
-    update_tile<kStoreM, false>(tl, a);
+    update_tile<kStoreM, false>(tl, g, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -463,7 +466,7 @@ __device__ __forceinline__ void materialize_tile(const Tile &tl, const Geometry 
     for (int c = 0; c < kPerLane; ++c)
       if (in_tile<kFull>(tl, ln, c)) a.e_w[off + 64 * c] = onebit_error(a.x_w[off + 64 * c], s);
   }
-  const float ss = a.scale_s[t];
+  const float ss = a.scale_s[g.tile_piece[blockIdx.x]];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     if (!in_tile<kFull>(tl, ln, c)) continue;
@@ -580,10 +583,12 @@ void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerAr
 }
 
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0, int nrows,
-                           float *out, hipStream_t s) {
-  const int64_t waves = static_cast<int64_t>(nrows) * g.T;
+                           const int32_t *begin, const int64_t *numel, int count, float *out,
+                           hipStream_t s) {
+  const int64_t waves = static_cast<int64_t>(nrows) * count;
   const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves)), block(kBlock);
-  hipLaunchKernelGGL(scale_finalize, grid, block, 0, s, g, partials, row0, nrows, out);
+  hipLaunchKernelGGL(scale_finalize, grid, block, 0, s, g, partials, row0, nrows, begin, numel,
+                     count, out);
 }
 
 template <bool kPow2>

@@ -36,7 +36,8 @@
  * Per-worker buffers are [W][N] with row stride N.  A packed sign message is
  * uint64 words, Nw = N/64 per worker: word j, bit k holds element 64*j + k;
  * each tensor starts on a word; bits past a tensor's end are written as 0.
- * Scales are fp32: scale_w is [W][T] (row stride T), scale_s is [T].
+ * Scales are fp32: scale_w is [W][T] (row stride T), scale_s is [S]: one
+ * per tensor (S = T) unless the server is partitioned (ob_set_server_chunks).
  *
  * Ownership.  The caller owns every buffer passed in: device memory (HBM)
  * pointers, each aligned to 16 bytes.  The library owns only the context and
@@ -179,6 +180,19 @@ int ob_warmup_step(ob_ctx *ctx, const void *grads, float *m, float *v, float *pa
  * element of err_w [W][N] and err_s [N] (padding untouched).  The next step
  * is ob_step, or ob_step_residual with first != 0. */
 int ob_begin_compression(ob_ctx *ctx, float *err_w, float *err_s, void *stream);
+
+/* Partitioned server: when the server role is split C ways, rank j holds
+ * chunk j of every tensor and compresses it with its own scale.  Chunk j of
+ * an n-element tensor covers elements [j*S_t, min((j+1)*S_t, n)) with
+ * S_t = 8192*ceil(ceil(n/8192)/C) (whole 8192-element blocks, so a chunk
+ * boundary never splits a sign word); a tensor has ceil(n/S_t) <= C chunks.
+ * After this call every server scale (scale_s, the server message) is per
+ * chunk, in tensor order then chunk order; ob_server_scale_count gives their
+ * number S.  C = 1 (the default) is one scale per tensor.  Synchronous (waits
+ * for the device, then uploads small tables); changes of C between steps
+ * also change what scale_s holds, so use it before the first step. */
+int ob_set_server_chunks(ob_ctx *ctx, int32_t chunks);
+int32_t ob_server_scale_count(const ob_ctx *ctx);
 
 /* Kernel timing for measurement.  With profiling on, every kernel the context
  * launches is bracketed by HIP events on its stream.  ob_profile_read waits for

@@ -47,6 +47,12 @@ The pages give no formulas.  The readings taken where they are silent:
   R10 warmup (uncompressed Adam): gbar = fp32 average of the W gradients as in
       R6; m <- c1*m + c2*gbar; v <- fp32(b2)*v + fp32(1 - b2)*(gbar*gbar);
       p <- p - lr*(m/(sqrt(v)+eps)); no bias correction.
+  R11 partitioned server (optional, C chunks): when the server role is split
+      C ways, rank j holds chunk j of every tensor and gives it its own scale.
+      Chunk j of an n-element tensor covers [j*S, min((j+1)*S, n)) with
+      S = 8192 * ceil(ceil(n / 8192) / C): whole 8192-element blocks, so no
+      chunk boundary splits a sign word; a tensor has ceil(n / S) <= C chunks.
+      C = 1 is the per-tensor scale of R4.
 
 All floating point below is numpy float32 (IEEE binary32, round to nearest
 even; numpy never contracts a*b+c) except the scale, which is fp64 as R1 says.
@@ -172,6 +178,46 @@ class OneBitCompressor:
         return np.where(unpack_signs(msg.words, msg.n), s, -s).astype(np.float32)
 
 
+CHUNK_BLOCK = 8192
+
+
+def chunk_bounds(n: int, chunks: int) -> List[Tuple[int, int]]:
+    """Element ranges of the server chunks of an n-element tensor (R11)."""
+    blocks = -(-n // CHUNK_BLOCK)
+    size = CHUNK_BLOCK * -(-blocks // chunks)
+    return [(lo, min(lo + size, n)) for lo in range(0, n, size)]
+
+
+@dataclass
+class ChunkedMessage:
+    """Packed sign words of the whole tensor plus one fp32 scale per chunk."""
+    words: np.ndarray
+    scales: np.ndarray   # fp32 [chunks]
+    bounds: List[Tuple[int, int]]
+    n: int
+
+
+class ChunkedOneBitCompressor:
+    """The 1-bit compressor applied chunk by chunk (R11): signs of every
+    element, one scale per chunk."""
+
+    def __init__(self, chunks: int):
+        self.chunks = chunks
+
+    def compress(self, x: np.ndarray) -> ChunkedMessage:
+        bounds = chunk_bounds(x.size, self.chunks)
+        scales = np.array([onebit_scale(x[lo:hi]) for lo, hi in bounds], dtype=np.float32)
+        return ChunkedMessage(pack_signs(sign_bits(x)), scales, bounds, x.size)
+
+    @staticmethod
+    def decompress(msg: ChunkedMessage) -> np.ndarray:
+        bits = unpack_signs(msg.words, msg.n)
+        out = np.empty(msg.n, dtype=np.float32)
+        for (lo, hi), s in zip(msg.bounds, msg.scales):
+            out[lo:hi] = np.where(bits[lo:hi], s, -s)
+        return out
+
+
 class IdentityCompressor:
     """No compression: the message is the value itself.  With it the step must
     reduce to preconditioned momentum SGD."""
@@ -232,14 +278,17 @@ class StepOutput:
 
 
 def compression_step(st: TensorState, grads: np.ndarray, beta1: float, lr: float,
-                     eps: float, comp=OneBitCompressor) -> StepOutput:
+                     eps: float, comp=OneBitCompressor, server_comp=None) -> StepOutput:
     """One compression-phase step of one tensor.
 
     grads is [W][n] (fp32, or bf16 as uint16 bit patterns).  Order:
     per worker w (each independent): m_w, x_w = m_w + e_w, message and new e_w;
     server: y = average of the messages, z = y + e_s, message and new e_s;
     m <- decompress(server message); p <- preconditioned update with m.
+    server_comp (default: comp) compresses the server's value, for example
+    ChunkedOneBitCompressor(C) for a C-way partitioned server (R11).
     """
+    scomp = comp if server_comp is None else server_comp
     W = grads.shape[0]
     msgs = []
     err_w = np.empty_like(st.err_w)
@@ -248,8 +297,8 @@ def compression_step(st: TensorState, grads: np.ndarray, beta1: float, lr: float
         msg, err_w[w] = error_compensated_compress(x, comp)
         msgs.append(msg)
     z = server_average(msgs, comp) + st.err_s
-    smsg, err_s = error_compensated_compress(z, comp)
-    m = comp.decompress(smsg).astype(np.float32)
+    smsg, err_s = error_compensated_compress(z, scomp)
+    m = scomp.decompress(smsg).astype(np.float32)
     p = preconditioned_update(st.p, m, st.v, lr, eps)
     return StepOutput(TensorState(p, m, st.v, err_s, err_w), msgs, smsg)
 

@@ -80,11 +80,20 @@ def _cmp_words(name: str, got: np.ndarray, ref: np.ndarray, rep: Report):
 class Run:
     """Device buffers for one tensor list plus the library context."""
 
-    def __init__(self, wl: Workload, device="cuda", state: Optional[Dict[str, torch.Tensor]] = None):
+    def __init__(self, wl: Workload, device="cuda", state: Optional[Dict[str, torch.Tensor]] = None,
+                 server_chunks: int = 1):
         from error_compensated_bit_02_amd import OneBitAdam
         from synth import init_state
         self.wl = wl
         self.ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
+        self.server_chunks = server_chunks
+        if server_chunks != 1:
+            self.ctx.set_server_chunks(server_chunks)
+        counts = [len(ob.chunk_bounds(n, server_chunks)) for n in wl.numel]
+        self.piece_base = [0]
+        for k in counts:
+            self.piece_base.append(self.piece_base[-1] + k)
+        assert self.ctx.S == self.piece_base[-1]
         self.off, self.N = padded_layout(wl.numel)
         assert self.ctx.offsets == self.off
         self.state = init_state(wl, device) if state is None else state
@@ -143,8 +152,10 @@ class Run:
         _cmp_words(f"{what} packed_w", _u64(b["packed_w"][:, wlo:whi]).ravel(), ref_w.ravel(), rep)
         _cmp_words(f"{what} packed_s", _u64(b["packed_s"][wlo:whi]), out.server_msg.words, rep)
         _cmp_float(f"{what} scale_w", b["scale_w"][:, t].cpu().numpy(), ref_sw, rep, rtol=SCALE_RTOL)
-        _cmp_float(f"{what} scale_s", b["scale_s"][t:t + 1].cpu().numpy(),
-                   np.array([out.server_msg.scale], np.float32), rep, rtol=SCALE_RTOL)
+        ref_ss = (out.server_msg.scales if isinstance(out.server_msg, ob.ChunkedMessage)
+                  else np.array([out.server_msg.scale], np.float32))
+        got_ss = b["scale_s"][self.piece_base[t]:self.piece_base[t + 1]].cpu().numpy()
+        _cmp_float(f"{what} scale_s", got_ss, ref_ss, rep, rtol=SCALE_RTOL)
         st = out.state
         _cmp_float(f"{what} err_w", host_slice(s["err_w"], lo, hi), st.err_w, rep, atol=STATE_ATOL)
         _cmp_float(f"{what} err_s", host_slice(s["err_s"], lo, hi), st.err_s, rep, atol=STATE_ATOL)
@@ -152,15 +163,21 @@ class Run:
         _cmp_float(f"{what} p", host_slice(s["p"], lo, hi), st.p, rep, atol=STATE_ATOL)
 
 
+def oracle_step(st, g, wl: Workload, server_chunks: int = 1) -> ob.StepOutput:
+    scomp = None if server_chunks == 1 else ob.ChunkedOneBitCompressor(server_chunks)
+    return ob.compression_step(st, g, wl.beta1, wl.lr, wl.eps, server_comp=scomp)
+
+
 def parity_run(wl: Workload, steps: int, tensors: Optional[Sequence[int]] = None,
                grads_fn=None, split: bool = False, device="cuda",
-               state: Optional[Dict[str, torch.Tensor]] = None, residual: bool = False) -> Report:
+               state: Optional[Dict[str, torch.Tensor]] = None, residual: bool = False,
+               server_chunks: int = 1) -> Report:
     """Run `steps` steps on the device and on the oracle for `tensors` (all by
     default), comparing after every step.  grads_fn(step) -> [W][N] device tensor.
     residual=True runs the residual-form step and compares its materialized state."""
     from synth import grads_for_step
     tensors = list(range(wl.num_tensors)) if tensors is None else list(tensors)
-    run = Run(wl, device, state)
+    run = Run(wl, device, state, server_chunks=server_chunks)
     ref = run.host_state(tensors)
     rep = Report()
     gbuf = None
@@ -180,7 +197,7 @@ def parity_run(wl: Workload, steps: int, tensors: Optional[Sequence[int]] = None
             (run.step_split if split else run.step)(g)
         torch.cuda.synchronize()
         for i, t in enumerate(tensors):
-            out = ob.compression_step(ref[i], host_g[i], wl.beta1, wl.lr, wl.eps)
+            out = oracle_step(ref[i], host_g[i], wl, server_chunks)
             run.compare(t, out, rep, f"{wl.name} step {k} tensor {t}", state=view)
             ref[i] = out.state
         log(f"  {wl.name} step {k}: ok ({time.time() - t0:.1f}s, {len(tensors)} tensors)")

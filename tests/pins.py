@@ -410,4 +410,60 @@ def pin_message_format_accounting():
     assert abs(4 * n / ob.message_bytes(n) - 32.0) < 0.01
 
 
+def pin_chunk_partition():
+    """Chunks tile each tensor exactly once, in whole 8192-element blocks (the
+    last may be shorter), at most C of them, and C = 1 is the whole tensor."""
+    for n in (1, 64, 8191, 8192, 8193, 20000, 100003, 1 << 20):
+        assert ob.chunk_bounds(n, 1) == [(0, n)]
+        for C in (2, 3, 4, 8, 64):
+            b = ob.chunk_bounds(n, C)
+            assert b[0][0] == 0 and b[-1][1] == n and len(b) <= C
+            assert all(b[i][1] == b[i + 1][0] for i in range(len(b) - 1))
+            assert all((hi - lo) % 8192 == 0 for lo, hi in b[:-1])
+            assert len({hi - lo for lo, hi in b[:-1]}) <= 1
+    # C chunks of a tensor of exactly C blocks are the blocks themselves
+    assert ob.chunk_bounds(4 * 8192, 4) == [(i * 8192, (i + 1) * 8192) for i in range(4)]
+
+
+def pin_chunked_scales_closed_form():
+    """With |x| = a_j on chunk j, chunk j's scale is a_j and the error is 0;
+    with one chunk the message equals the per-tensor message."""
+    rng = _rng(17)
+    n, C = 3 * 8192 + 100, 4
+    bounds = ob.chunk_bounds(n, C)
+    mags = [np.float32(0.5), np.float32(3.0), np.float32(1e-3), np.float32(7.25)]
+    x = np.empty(n, np.float32)
+    for (lo, hi), a in zip(bounds, mags):
+        x[lo:hi] = np.where(rng.random(hi - lo) < 0.5, a, -a)
+    comp = ob.ChunkedOneBitCompressor(C)
+    msg, e = ob.error_compensated_compress(x, comp)
+    assert msg.scales.tolist() == [float(a) for a in mags[:len(bounds)]]
+    assert np.all(e == 0)
+    y = rng.standard_normal(n).astype(np.float32)
+    one = ob.ChunkedOneBitCompressor(1).compress(y)
+    ref = ob.OneBitCompressor.compress(y)
+    assert np.array_equal(one.words, ref.words) and one.scales[0] == ref.scale
+    assert np.array_equal(ob.ChunkedOneBitCompressor.decompress(one), ob.OneBitCompressor.decompress(ref))
+    # each chunk's scale is that chunk's own RMS
+    msg = comp.compress(y)
+    for (lo, hi), s in zip(msg.bounds, msg.scales):
+        assert s == ob.onebit_scale(y[lo:hi])
+
+
+def pin_chunked_server_step():
+    """A C-way partitioned server keeps the step's invariants: W = 1 at the
+    first step still leaves e_s = 0 when every chunk of the worker message
+    has one magnitude, and the server error telescopes."""
+    rng = _rng(18)
+    n = 2 * 8192 + 300
+    g = np.empty((1, n), np.float32)
+    g[0] = np.where(rng.random(n) < 0.5, 1.0, -1.0).astype(np.float32)
+    st = ob.TensorState(np.zeros(n, np.float32), np.zeros(n, np.float32), np.ones(n, np.float32),
+                        np.zeros(n, np.float32), np.zeros((1, n), np.float32))
+    out = ob.compression_step(st, g, 0.9, 1e-4, 1e-8, server_comp=ob.ChunkedOneBitCompressor(3))
+    assert np.all(out.state.err_s == 0)
+    assert len(out.server_msg.scales) == 3
+    assert np.all(np.abs(out.state.m) == out.worker_msgs[0].scale)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

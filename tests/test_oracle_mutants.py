@@ -106,6 +106,17 @@ def _warmup_v_linear(st, grads, beta1, beta2, lr, eps):
 MUTANTS["warmup_v_not_squared"] = ("warmup_step", _warmup_v_linear)
 
 
+def _chunks_off_by_one_block(n, chunks):
+    blocks = -(-n // ob.CHUNK_BLOCK)
+    size = ob.CHUNK_BLOCK * max(1, -(-blocks // chunks) - (1 if blocks > chunks else 0))
+    return [(lo, min(lo + size, n)) for lo in range(0, n, size)]
+
+
+MUTANTS["chunk_size_one_block_short"] = ("chunk_bounds", _chunks_off_by_one_block)
+MUTANTS["chunk_bounds_not_block_aligned"] = ("chunk_bounds",
+    lambda n, c: [(lo, min(lo + -(-n // c), n)) for lo in range(0, n, -(-n // c))])
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
