@@ -55,6 +55,9 @@ def kernel_bytes_per_element(wl) -> dict:
         "worker_pass2": 4.0 + (g + 4.0) * W + 4.0 * W,        # read m, g, e; write e
         "server_pass1": W / 8.0 + 4.0,                        # read signs, e_s
         "server_pass2_update": W / 8.0 + 16.0 + 12.0 + 1 / 8.0,  # read signs, e_s, v, p; write e_s, m, p, signs
+        "server_pass2": W / 8.0 + 8.0 + 1 / 8.0,              # read signs, e_s; write e_s, signs
+        "apply_update": 1 / 8.0 + 16.0,                       # read signs, v, p; write m, p
+        "trust_norms": 1 / 8.0 + 8.0,                         # read signs, v, p
         # residual form: read g, x_prev and the previous server signs (the momentum); write x, signs
         "worker_residual": (g + 8.0) * W + W / 8.0 + 1 / 8.0,
         "server_residual": W / 8.0 + 8.0 + 1 / 8.0,           # read signs, z_prev; write z, server signs
@@ -184,6 +187,8 @@ def main() -> int:
                     help="state form between steps; both forms give bit-identical trajectories. "
                          "'both' times the residual form (the headline) and the strict form")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct gradient sets cycled")
+    ap.add_argument("--trust-ratio", type=float, default=None, metavar="WD",
+                    help="layer-wise trust-ratio update with weight decay WD")
     ap.add_argument("--server-chunks", type=int, default=1,
                     help="partitioned server: one server scale per tensor chunk (1 = per tensor)")
     ap.add_argument("--cpu-sample-tensors", type=int, default=64)
@@ -222,6 +227,8 @@ def main() -> int:
     ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
     if args.server_chunks != 1:
         ctx.set_server_chunks(args.server_chunks)
+    if args.trust_ratio is not None:
+        ctx.set_trust_ratio(True, args.trust_ratio)
     sets = max(1, min(args.grad_sets, args.steps + args.warmup))
     grads = [grads_for_step(wl, k, "cuda") for k in range(sets)]
     torch.cuda.synchronize()
@@ -245,7 +252,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "tensors": wl.num_tensors, "elements": n_elem,
                    "workers": wl.workers, "grad_dtype": wl.grad_dtype,
-                   "grad_sets": sets, "state_form": forms[0], "server_chunks": args.server_chunks},
+                   "grad_sets": sets, "state_form": forms[0], "server_chunks": args.server_chunks,
+                   "trust_ratio_weight_decay": args.trust_ratio},
         "step_hbm_gbps_algorithmic": head["step_hbm_gbps_algorithmic"],
         "step_frac_of_peak": head["step_frac_of_peak"],
         "step_bytes_per_element": step_bytes_per_element(wl),

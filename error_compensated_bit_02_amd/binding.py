@@ -39,6 +39,7 @@ SIGNATURES = {
     "ob_begin_compression": (ctypes.c_int, [_c_void_p] * 4),
     "ob_set_server_chunks": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_server_scale_count": (_i32, [_c_void_p]),
+    "ob_set_trust_ratio": (ctypes.c_int, [_c_void_p, _i32, _f64]),
     "ob_profile_enable": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_profile_kinds": (_i32, []),
     "ob_profile_kind_name": (ctypes.c_char_p, [_i32]),
@@ -129,6 +130,11 @@ class OneBitAdam:
                "ob_init")
         self._ctx = ctx
         self.S = self.lib.ob_server_scale_count(self._ctx)
+
+    def set_trust_ratio(self, enable: bool, weight_decay: float = 0.0) -> None:
+        """Scale each tensor's update by its trust ratio ||p|| / ||u||; see include/ob.h."""
+        _check(self.lib.ob_set_trust_ratio(self._ctx, 1 if enable else 0, float(weight_decay)),
+               "ob_set_trust_ratio")
 
     def set_server_chunks(self, chunks: int) -> None:
         """Partition the server C ways (one scale per tensor chunk); see include/ob.h."""

@@ -35,6 +35,9 @@ struct ob_ctx {
   std::vector<int32_t> tile_begin;   // host copy [T+1]
   int32_t server_chunks = 1;
   int32_t S = 0;                     // server scales (pieces)
+  bool trust_ratio = false;          // layer-wise trust-ratio update
+  float weight_decay = 0.0f;
+  float *d_ratio = nullptr;          // [T] trust ratios (device scratch)
   int32_t *d_tile_piece = nullptr;   // device views into scratch
   int32_t *d_piece_begin = nullptr;
   int64_t *d_piece_numel = nullptr;
@@ -51,7 +54,8 @@ namespace {
 const char *const kKindNames[ob::K_NUM_KINDS] = {
     "worker_pass1", "scale_finalize", "worker_pass2", "server_pass1",
     "server_pass2", "server_pass2_update", "apply_update", "worker_residual",
-    "server_residual", "update_residual", "materialize", "warmup", "zero_errors"};
+    "server_residual", "update_residual", "materialize", "warmup", "zero_errors",
+    "trust_norms", "trust_ratio"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -158,6 +162,22 @@ int do_server_first(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, f
     ob::launch_scale_finalize(g, c->partials, c->W, 1, g.piece_begin, g.piece_numel, c->S,
                               scale_s, s);
   });
+}
+
+// The update from the server message: plain, or scaled per tensor by the
+// trust ratio (two more launches: per-tile norms, per-tensor ratios).
+int do_update(ob_ctx *c, bool store_m, ob::Kind kind, const uint64_t *packed_s,
+              const float *scale_s, const float *v, float *m, float *params, double lr,
+              hipStream_t s) {
+  const ob::UpdateArgs a{packed_s, scale_s, v, m, params, static_cast<float>(lr), c->eps,
+                         c->d_ratio, c->weight_decay};
+  if (c->trust_ratio) {
+    int st = timed(c, ob::K_TRUST_NORMS, s, [&] { ob::launch_trust_norms(c->geo, a, c->partials, s); });
+    if (st) return st;
+    st = timed(c, ob::K_TRUST_RATIO, s, [&] { ob::launch_trust_ratio(c->geo, c->partials, c->d_ratio, s); });
+    if (st) return st;
+  }
+  return timed(c, kind, s, [&] { ob::launch_update(store_m, c->trust_ratio, c->geo, a, s); });
 }
 
 // Server pieces for a C-way partitioned server: chunk j of tensor t is a run
@@ -274,6 +294,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   const size_t b_pbegin = up((tiles.size() + 1) * sizeof(int32_t));
   const size_t b_pnumel = up(tiles.size() * sizeof(int64_t));
   const size_t b_pieces = b_tpiece + b_pbegin + b_pnumel;
+  const size_t b_ratio = up(c->numel.size() * sizeof(float));
   const size_t b_part =
       up(ob::partials_count(num_workers, static_cast<int>(tiles.size())) * sizeof(double2));
   std::vector<unsigned char> host(b_tiles + b_begin + b_numel, 0);
@@ -285,7 +306,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   std::copy(reinterpret_cast<const unsigned char *>(c->numel.data()),
             reinterpret_cast<const unsigned char *>(c->numel.data() + c->numel.size()),
             host.data() + b_tiles + b_begin);
-  if (hipMalloc(&c->scratch, host.size() + b_pieces + b_part) != hipSuccess) {
+  if (hipMalloc(&c->scratch, host.size() + b_pieces + b_ratio + b_part) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return OB_ERR_NOMEM;
@@ -306,7 +327,8 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->geo.tile_piece = c->d_tile_piece;
   c->geo.piece_begin = c->d_piece_begin;
   c->geo.piece_numel = c->d_piece_numel;
-  c->partials = reinterpret_cast<double2 *>(pieces + b_pieces);
+  c->d_ratio = reinterpret_cast<float *>(pieces + b_pieces);
+  c->partials = reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio);
   c->geo.num_tiles = c->num_tiles;
   c->geo.T = c->T;
   c->geo.W = c->W;
@@ -365,8 +387,7 @@ int ob_apply_update(ob_ctx *c, const uint64_t *packed_s, const float *scale_s, c
   const int st = check_ptrs(packed_s, scale_s, v, m, params);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const ob::UpdateArgs a{packed_s, scale_s, v, m, params, static_cast<float>(lr), c->eps};
-  return timed(c, ob::K_APPLY_UPDATE, s, [&] { ob::launch_update(true, c->geo, a, s); });
+  return do_update(c, true, ob::K_APPLY_UPDATE, packed_s, scale_s, v, m, params, lr, s);
 }
 
 int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *params, float *err_w,
@@ -380,6 +401,14 @@ int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *param
   if (r) return r;
   r = do_server_first(c, packed_w, scale_w, err_s, scale_s, s);
   if (r) return r;
+  if (c->trust_ratio) {   // the ratio needs the whole tensor's update: no fusion
+    const ob::ServerArgs a = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
+    r = timed(c, ob::K_SERVER_PASS2, s, [&] {
+      ob::launch_server(ob::ServerPass::kStrictErrors, c->geo, a, s);
+    });
+    if (r) return r;
+    return do_update(c, true, ob::K_APPLY_UPDATE, packed_s, scale_s, v, m, params, lr, s);
+  }
   ob::ServerArgs a = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
   a.v = v;
   a.m = m;
@@ -421,8 +450,7 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
                               scale_s, s);
   });
   if (r) return r;
-  const ob::UpdateArgs ua{packed_s, scale_s, v, nullptr, params, static_cast<float>(lr), c->eps};
-  return timed(c, ob::K_UPDATE_RESIDUAL, s, [&] { ob::launch_update(false, g, ua, s); });
+  return do_update(c, false, ob::K_UPDATE_RESIDUAL, packed_s, scale_s, v, nullptr, params, lr, s);
 }
 
 int ob_materialize(ob_ctx *c, const float *x_w, const float *scale_w, const float *z,
@@ -462,6 +490,13 @@ int ob_set_server_chunks(ob_ctx *c, int32_t chunks) {
 }
 
 int32_t ob_server_scale_count(const ob_ctx *c) { return c == nullptr ? -1 : c->S; }
+
+int ob_set_trust_ratio(ob_ctx *c, int32_t enable, double weight_decay) {
+  if (c == nullptr || !std::isfinite(weight_decay) || weight_decay < 0.0) return OB_ERR_INVALID;
+  c->trust_ratio = enable != 0;
+  c->weight_decay = static_cast<float>(weight_decay);
+  return OB_OK;
+}
 
 int ob_profile_enable(ob_ctx *c, int32_t enable) {
   if (c == nullptr) return OB_ERR_INVALID;

@@ -71,6 +71,8 @@ enum Kind {
   K_MATERIALIZE,
   K_WARMUP,
   K_ZERO_ERRORS,
+  K_TRUST_NORMS,
+  K_TRUST_RATIO,
   K_NUM_KINDS
 };
 
@@ -124,6 +126,8 @@ struct UpdateArgs {
   float *m;                  // written when the momentum is stored
   float *params;
   float lr, eps;
+  const float *ratio;        // [T] per-tensor trust ratios (trust-ratio update only)
+  float wd;                  // weight decay added to the direction (trust-ratio update only)
 };
 
 struct MaterializeArgs {     // inputs and outputs may alias
@@ -152,7 +156,12 @@ void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0,
                            const int32_t *begin, const int64_t *numel, int count, float *out,
                            hipStream_t s);
 void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s);
-void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStream_t s);
+// with_ratio: p -= lr * (ratio[t] * u), u = m / (sqrt(v) + eps) (+ wd * p)
+void launch_update(bool store_m, bool with_ratio, const Geometry &g, const UpdateArgs &a,
+                   hipStream_t s);
+// Per-tile sums of p^2 and u^2 into partial rows 0 and 1, then per-tensor ratios.
+void launch_trust_norms(const Geometry &g, const UpdateArgs &a, double2 *partials, hipStream_t s);
+void launch_trust_ratio(const Geometry &g, const double2 *partials, float *ratio, hipStream_t s);
 void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s);
 void launch_warmup(const Geometry &g, bool bf16, const WarmupArgs &a, hipStream_t s);
 void launch_zero_errors(const Geometry &g, float *err_w, float *err_s, hipStream_t s);

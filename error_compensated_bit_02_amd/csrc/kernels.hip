@@ -416,10 +416,11 @@ __global__ __launch_bounds__(kBlock) void server_kernel(Geometry g, ServerArgs a
 // update from a server message: m = s_s*sign (stored if kStoreM),
 // p <- p - lr * (m / (sqrt(v) + eps))
 // ---------------------------------------------------------------------------
-template <bool kStoreM, bool kFull>
+template <bool kStoreM, bool kRatio, bool kFull>
 __device__ __forceinline__ void update_tile(const Tile &tl, const Geometry &g, const UpdateArgs &a) {
   const Lanes ln = lanes_of<kFull>(tl);
   const float ss = a.scale_s[g.tile_piece[blockIdx.x]];
+  const float r = kRatio ? a.ratio[tl.tensor] : 1.0f;
   const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
   float vv[kPerLane], pv[kPerLane];
 #pragma unroll
@@ -434,19 +435,90 @@ __device__ __forceinline__ void update_tile(const Tile &tl, const Geometry &g, c
     if (!in_tile<kFull>(tl, ln, c)) continue;
     const int64_t i = ln.base + 64 * c + ln.lane;
     const float d = __builtin_sqrtf(vv[c]) + a.eps;
-    const float u = mv / d;
+    float u = mv / d;
     if (kStoreM) a.m[i] = mv;
-    a.params[i] = pv[c] - a.lr * u;
+    if (kRatio) {
+      if (a.wd > 0.0f) u = u + a.wd * pv[c];
+      a.params[i] = pv[c] - a.lr * (r * u);
+    } else {
+      a.params[i] = pv[c] - a.lr * u;
+    }
   }
 }
 
-template <bool kStoreM>
+template <bool kStoreM, bool kRatio>
 __global__ __launch_bounds__(kBlock) void update_kernel(Geometry g, UpdateArgs a) {
   const Tile tl = g.tiles[blockIdx.x];
   if (tl.len == kTile)
-    update_tile<kStoreM, true>(tl, g, a);
+    update_tile<kStoreM, kRatio, true>(tl, g, a);
   else
-    update_tile<kStoreM, false>(tl, g, a);
+    update_tile<kStoreM, kRatio, false>(tl, g, a);
+}
+
+// ---------------------------------------------------------------------------
+// trust ratio: per tile, compensated sums of p^2 and u^2 (partial rows 0, 1);
+// per tensor, r = fp32(sqrt(sum p^2) / sqrt(sum u^2)), 1 when either is 0
+// ---------------------------------------------------------------------------
+template <bool kFull>
+__device__ __forceinline__ void trust_norms_tile(const Tile &tl, const Geometry &g,
+                                                 const UpdateArgs &a, const PartialSink &sink) {
+  const Lanes ln = lanes_of<kFull>(tl);
+  const float ss = a.scale_s[g.tile_piece[blockIdx.x]];
+  const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
+  double ph = 0.0, pl = 0.0, uh = 0.0, ul = 0.0;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    const float mv = signed_scale(words, c, ss);
+    const bool ok = in_tile<kFull>(tl, ln, c);
+    const float vv = ok ? a.v[ln.base + 64 * c + ln.lane] : 0.0f;
+    const float pv = ok ? a.params[ln.base + 64 * c + ln.lane] : 0.0f;
+    const float d = __builtin_sqrtf(vv) + a.eps;
+    float u = mv / d;
+    if (a.wd > 0.0f) u = u + a.wd * pv;
+    dd_accumulate(ph, pl, pv);
+    dd_accumulate(uh, ul, ok ? u : 0.0f);
+  }
+  park_partial(sink, 0, ln.wave, ph, pl);
+  park_partial(sink, 1, ln.wave, uh, ul);
+  flush_partials(sink, 0, 2);
+}
+
+__global__ __launch_bounds__(kBlock) void trust_norms_kernel(Geometry g, UpdateArgs a,
+                                                             double2 *partials) {
+  __shared__ double2 red[2][kWaves];
+  const PartialSink sink{red, partials, g.num_tiles, static_cast<int>(blockIdx.x)};
+  const Tile tl = g.tiles[blockIdx.x];
+  if (tl.len == kTile)
+    trust_norms_tile<true>(tl, g, a, sink);
+  else
+    trust_norms_tile<false>(tl, g, a, sink);
+}
+
+__global__ __launch_bounds__(kBlock) void trust_ratio_kernel(Geometry g,
+                                                             const double2 *__restrict__ partials,
+                                                             float *__restrict__ ratio) {
+  const int lane = threadIdx.x & 63;
+  const int t = static_cast<int>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (t >= g.T) return;  // whole wavefront leaves together
+  double sum[2];
+#pragma unroll
+  for (int row = 0; row < 2; ++row) {
+    const double2 *p = partials + static_cast<size_t>(row) * g.num_tiles;
+    double hi = 0.0, lo = 0.0;
+    for (int i = g.tile_begin[t] + lane; i < g.tile_begin[t + 1]; i += 64) dd_add(hi, lo, p[i].x, p[i].y);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const double oh = __shfl_xor(hi, d);
+      const double ol = __shfl_xor(lo, d);
+      dd_add(hi, lo, oh, ol);
+    }
+    sum[row] = hi + lo;
+  }
+  if (lane == 0) {
+    ratio[t] = (sum[0] == 0.0 || sum[1] == 0.0)
+                   ? 1.0f
+                   : static_cast<float>(__builtin_sqrt(sum[0]) / __builtin_sqrt(sum[1]));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -615,12 +687,26 @@ void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipS
     launch_server_w<false>(pass, g, a, s);
 }
 
-void launch_update(bool store_m, const Geometry &g, const UpdateArgs &a, hipStream_t s) {
+void launch_update(bool store_m, bool with_ratio, const Geometry &g, const UpdateArgs &a,
+                   hipStream_t s) {
   const dim3 grid(g.num_tiles), block(kBlock);
-  if (store_m)
-    hipLaunchKernelGGL(update_kernel<true>, grid, block, 0, s, g, a);
+  if (store_m && with_ratio)
+    hipLaunchKernelGGL((update_kernel<true, true>), grid, block, 0, s, g, a);
+  else if (store_m)
+    hipLaunchKernelGGL((update_kernel<true, false>), grid, block, 0, s, g, a);
+  else if (with_ratio)
+    hipLaunchKernelGGL((update_kernel<false, true>), grid, block, 0, s, g, a);
   else
-    hipLaunchKernelGGL(update_kernel<false>, grid, block, 0, s, g, a);
+    hipLaunchKernelGGL((update_kernel<false, false>), grid, block, 0, s, g, a);
+}
+
+void launch_trust_norms(const Geometry &g, const UpdateArgs &a, double2 *partials, hipStream_t s) {
+  hipLaunchKernelGGL(trust_norms_kernel, dim3(g.num_tiles), dim3(kBlock), 0, s, g, a, partials);
+}
+
+void launch_trust_ratio(const Geometry &g, const double2 *partials, float *ratio, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((g.T + kWaves - 1) / kWaves)), block(kBlock);
+  hipLaunchKernelGGL(trust_ratio_kernel, grid, block, 0, s, g, partials, ratio);
 }
 
 void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t s) {

@@ -194,6 +194,19 @@ int ob_begin_compression(ob_ctx *ctx, float *err_w, float *err_s, void *stream);
 int ob_set_server_chunks(ob_ctx *ctx, int32_t chunks);
 int32_t ob_server_scale_count(const ob_ctx *ctx);
 
+/* Layer-wise trust ratio (the fugumt page on "1-bit LAMB": LAMB's layer-wise
+ * adaptive learning rates kept under compressed communication; the page gives
+ * no formula, this is the plainest reading).  With enable != 0 every update of
+ * this context (ob_step, ob_step_residual, ob_apply_update) becomes, per
+ * tensor t:
+ *   u[i] = m[i] / (sqrt(v[i]) + eps)   (+ fp32(weight_decay) * p[i] if > 0)
+ *   r_t  = fp32( sqrt(fl64(sum p^2)) / sqrt(fl64(sum u^2)) ), 1 if a sum is 0
+ *   p[i] = p[i] - lr * (r_t * u[i])
+ * with the sums exact up to one rounding, as for the scales.  It costs two
+ * more launches per step (the ratio needs the whole tensor's update) and one
+ * more read of v and params.  weight_decay >= 0 and finite. */
+int ob_set_trust_ratio(ob_ctx *ctx, int32_t enable, double weight_decay);
+
 /* Kernel timing for measurement.  With profiling on, every kernel the context
  * launches is bracketed by HIP events on its stream.  ob_profile_read waits for
  * the recorded events, writes per kernel kind the summed milliseconds and the

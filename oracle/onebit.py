@@ -53,6 +53,13 @@ The pages give no formulas.  The readings taken where they are silent:
       S = 8192 * ceil(ceil(n / 8192) / C): whole 8192-element blocks, so no
       chunk boundary splits a sign word; a tensor has ceil(n / S) <= C chunks.
       C = 1 is the per-tensor scale of R4.
+  R14 layer-wise trust ratio (optional; the fugumt page on "1-bit LAMB" says it
+      keeps LAMB's layer-wise adaptive learning rates under compressed
+      communication, with no formula): the compressed momentum m, the frozen
+      variance and the update direction u = m/(sqrt(v)+eps) (+ wd*p when a
+      weight decay wd > 0 is given) as in R8; per tensor the trust ratio
+      r = fp32(sqrt64(fl64(sum p^2)) / sqrt64(fl64(sum u^2))), r = 1 when either
+      sum is 0; p <- p - lr*(r*u).
 
 All floating point below is numpy float32 (IEEE binary32, round to nearest
 even; numpy never contracts a*b+c) except the scale, which is fp64 as R1 says.
@@ -253,6 +260,24 @@ def preconditioned_update(p: np.ndarray, m: np.ndarray, v: np.ndarray,
     return p - F32(lr) * (m / (np.sqrt(v) + F32(eps)))
 
 
+def trust_ratio(p: np.ndarray, u: np.ndarray) -> np.float32:
+    """LAMB's layer-wise trust ratio ||p|| / ||u|| of one tensor (R14)."""
+    sp, su = sum_of_squares(p), sum_of_squares(u)
+    if sp == 0.0 or su == 0.0:
+        return F32(1.0)
+    return F32(np.sqrt(np.float64(sp)) / np.sqrt(np.float64(su)))
+
+
+def trust_ratio_update(p: np.ndarray, m: np.ndarray, v: np.ndarray, lr: float, eps: float,
+                       weight_decay: float = 0.0) -> np.ndarray:
+    """The preconditioned update scaled per tensor by the trust ratio (R14)."""
+    u = m / (np.sqrt(v) + F32(eps))
+    if weight_decay > 0.0:
+        u = u + F32(weight_decay) * p
+    r = trust_ratio(p, u)
+    return p - F32(lr) * (r * u)
+
+
 # ---------------------------------------------------------------------------
 # one compression-phase step of one tensor, and of a tensor list
 # ---------------------------------------------------------------------------
@@ -278,7 +303,8 @@ class StepOutput:
 
 
 def compression_step(st: TensorState, grads: np.ndarray, beta1: float, lr: float,
-                     eps: float, comp=OneBitCompressor, server_comp=None) -> StepOutput:
+                     eps: float, comp=OneBitCompressor, server_comp=None,
+                     trust_ratio_wd=None) -> StepOutput:
     """One compression-phase step of one tensor.
 
     grads is [W][n] (fp32, or bf16 as uint16 bit patterns).  Order:
@@ -287,6 +313,8 @@ def compression_step(st: TensorState, grads: np.ndarray, beta1: float, lr: float
     m <- decompress(server message); p <- preconditioned update with m.
     server_comp (default: comp) compresses the server's value, for example
     ChunkedOneBitCompressor(C) for a C-way partitioned server (R11).
+    trust_ratio_wd, when not None, selects the trust-ratio update of R14 with
+    that weight decay.
     """
     scomp = comp if server_comp is None else server_comp
     W = grads.shape[0]
@@ -299,7 +327,10 @@ def compression_step(st: TensorState, grads: np.ndarray, beta1: float, lr: float
     z = server_average(msgs, comp) + st.err_s
     smsg, err_s = error_compensated_compress(z, scomp)
     m = scomp.decompress(smsg).astype(np.float32)
-    p = preconditioned_update(st.p, m, st.v, lr, eps)
+    if trust_ratio_wd is None:
+        p = preconditioned_update(st.p, m, st.v, lr, eps)
+    else:
+        p = trust_ratio_update(st.p, m, st.v, lr, eps, trust_ratio_wd)
     return StepOutput(TensorState(p, m, st.v, err_s, err_w), msgs, smsg)
 
 

@@ -81,7 +81,7 @@ class Run:
     """Device buffers for one tensor list plus the library context."""
 
     def __init__(self, wl: Workload, device="cuda", state: Optional[Dict[str, torch.Tensor]] = None,
-                 server_chunks: int = 1):
+                 server_chunks: int = 1, trust_wd: Optional[float] = None):
         from error_compensated_bit_02_amd import OneBitAdam
         from synth import init_state
         self.wl = wl
@@ -89,6 +89,8 @@ class Run:
         self.server_chunks = server_chunks
         if server_chunks != 1:
             self.ctx.set_server_chunks(server_chunks)
+        if trust_wd is not None:
+            self.ctx.set_trust_ratio(True, trust_wd)
         counts = [len(ob.chunk_bounds(n, server_chunks)) for n in wl.numel]
         self.piece_base = [0]
         for k in counts:
@@ -163,21 +165,23 @@ class Run:
         _cmp_float(f"{what} p", host_slice(s["p"], lo, hi), st.p, rep, atol=STATE_ATOL)
 
 
-def oracle_step(st, g, wl: Workload, server_chunks: int = 1) -> ob.StepOutput:
+def oracle_step(st, g, wl: Workload, server_chunks: int = 1,
+                trust_wd: Optional[float] = None) -> ob.StepOutput:
     scomp = None if server_chunks == 1 else ob.ChunkedOneBitCompressor(server_chunks)
-    return ob.compression_step(st, g, wl.beta1, wl.lr, wl.eps, server_comp=scomp)
+    return ob.compression_step(st, g, wl.beta1, wl.lr, wl.eps, server_comp=scomp,
+                               trust_ratio_wd=trust_wd)
 
 
 def parity_run(wl: Workload, steps: int, tensors: Optional[Sequence[int]] = None,
                grads_fn=None, split: bool = False, device="cuda",
                state: Optional[Dict[str, torch.Tensor]] = None, residual: bool = False,
-               server_chunks: int = 1) -> Report:
+               server_chunks: int = 1, trust_wd: Optional[float] = None) -> Report:
     """Run `steps` steps on the device and on the oracle for `tensors` (all by
     default), comparing after every step.  grads_fn(step) -> [W][N] device tensor.
     residual=True runs the residual-form step and compares its materialized state."""
     from synth import grads_for_step
     tensors = list(range(wl.num_tensors)) if tensors is None else list(tensors)
-    run = Run(wl, device, state, server_chunks=server_chunks)
+    run = Run(wl, device, state, server_chunks=server_chunks, trust_wd=trust_wd)
     ref = run.host_state(tensors)
     rep = Report()
     gbuf = None
@@ -197,7 +201,7 @@ def parity_run(wl: Workload, steps: int, tensors: Optional[Sequence[int]] = None
             (run.step_split if split else run.step)(g)
         torch.cuda.synchronize()
         for i, t in enumerate(tensors):
-            out = oracle_step(ref[i], host_g[i], wl, server_chunks)
+            out = oracle_step(ref[i], host_g[i], wl, server_chunks, trust_wd)
             run.compare(t, out, rep, f"{wl.name} step {k} tensor {t}", state=view)
             ref[i] = out.state
         log(f"  {wl.name} step {k}: ok ({time.time() - t0:.1f}s, {len(tensors)} tensors)")

@@ -466,4 +466,47 @@ def pin_chunked_server_step():
     assert np.all(np.abs(out.state.m) == out.worker_msgs[0].scale)
 
 
+def pin_trust_ratio():
+    """The trust ratio is the fp32 value nearest ||p|| / ||u|| (exact rational
+    midpoints), scales exactly with p, and is 1 for a zero tensor."""
+    rng = _rng(19)
+    for trial in range(40):
+        n = int(rng.integers(1, 300))
+        p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        u = (rng.standard_normal(n) * 10.0 ** rng.integers(-4, 2)).astype(np.float32)
+        r = ob.trust_ratio(p, u)
+        q2 = sum((frac(x) ** 2 for x in p), Fraction(0)) / sum((frac(x) ** 2 for x in u), Fraction(0))
+        lo, hi = np.nextafter(r, np.float32(0)), np.nextafter(r, np.float32(np.inf))
+        mid_lo, mid_hi = (frac(lo) + frac(r)) / 2, (frac(r) + frac(hi)) / 2
+        assert mid_lo ** 2 <= q2 <= mid_hi ** 2, trial
+        assert ob.trust_ratio(p * np.float32(8.0), u) == r * np.float32(8.0)
+        assert ob.trust_ratio(p, u * np.float32(0.25)) == r * np.float32(4.0)
+    assert ob.trust_ratio(np.zeros(5, np.float32), np.ones(5, np.float32)) == 1.0
+    assert ob.trust_ratio(np.ones(5, np.float32), np.zeros(5, np.float32)) == 1.0
+
+
+def pin_trust_ratio_update():
+    """p - lr*(r*u) with every fp32 operation rounded once, and when
+    ||p|| = ||u|| the ratio is 1 and the step is the plain preconditioned step."""
+    rng = _rng(20)
+    n = 200
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = np.exp(rng.standard_normal(n) * 2 - 14).astype(np.float32)
+    for wd in (0.0, 0.01):
+        out = ob.trust_ratio_update(p, m, v, 1e-3, 1e-8, wd)
+        u = np.array([f32_div(m[i], f32_add(f32_sqrt(v[i]), np.float32(1e-8))) for i in range(n)], np.float32)
+        if wd > 0:
+            u = np.array([f32_add(u[i], f32_mul(np.float32(wd), p[i])) for i in range(n)], np.float32)
+        r = ob.trust_ratio(p, u)
+        for i in range(n):
+            assert out[i] == f32_sub(p[i], f32_mul(np.float32(1e-3), f32_mul(r, u[i]))), (wd, i)
+    # |p_i| = |u_i| = 1 everywhere -> r = 1 -> identical to the plain step
+    ones = np.where(rng.random(n) < 0.5, 1.0, -1.0).astype(np.float32)
+    v1 = np.full(n, 0.25, np.float32)
+    m1 = ones * np.float32(0.5)          # u = m / (sqrt(v) + 0) = +-1 with eps = 0
+    assert np.array_equal(ob.trust_ratio_update(ones, m1, v1, 0.1, 0.0),
+                          ob.preconditioned_update(ones, m1, v1, 0.1, 0.0))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -117,6 +117,14 @@ MUTANTS["chunk_bounds_not_block_aligned"] = ("chunk_bounds",
     lambda n, c: [(lo, min(lo + -(-n // c), n)) for lo in range(0, n, -(-n // c))])
 
 
+MUTANTS["trust_ratio_inverted"] = ("trust_ratio", lambda p, u: F32(1.0) if (
+    ob.sum_of_squares(p) == 0 or ob.sum_of_squares(u) == 0) else F32(
+    np.sqrt(ob.sum_of_squares(u)) / np.sqrt(ob.sum_of_squares(p))))
+MUTANTS["trust_ratio_squared_norms"] = ("trust_ratio", lambda p, u: F32(1.0) if (
+    ob.sum_of_squares(p) == 0 or ob.sum_of_squares(u) == 0) else F32(
+    ob.sum_of_squares(p) / ob.sum_of_squares(u)))
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
