@@ -40,6 +40,9 @@ SIGNATURES = {
     "ob_set_server_chunks": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_server_scale_count": (_i32, [_c_void_p]),
     "ob_set_trust_ratio": (ctypes.c_int, [_c_void_p, _i32, _f64]),
+    "ob_cltk_configure": (ctypes.c_int, [_c_void_p, _f64, ctypes.POINTER(_i64)]),
+    "ob_cltk_layout": (ctypes.c_int, [_c_void_p, ctypes.POINTER(_i64)]),
+    "ob_cltk_step": (ctypes.c_int, [_c_void_p, _i64] + [_c_void_p] * 5 + [_c_void_p]),
     "ob_profile_enable": (ctypes.c_int, [_c_void_p, _i32]),
     "ob_profile_kinds": (_i32, []),
     "ob_profile_kind_name": (ctypes.c_char_p, [_i32]),
@@ -135,6 +138,24 @@ class OneBitAdam:
         """Scale each tensor's update by its trust ratio ||p|| / ||u||; see include/ob.h."""
         _check(self.lib.ob_set_trust_ratio(self._ctx, 1 if enable else 0, float(weight_decay)),
                "ob_set_trust_ratio")
+
+    def cltk_configure(self, density: float) -> List[int]:
+        """Set up the cyclic local top-k codec; returns k_off[0..T] (K = k_off[T])."""
+        K = _i64()
+        _check(self.lib.ob_cltk_configure(self._ctx, float(density), ctypes.byref(K)), "ob_cltk_configure")
+        out = (_i64 * (self.T + 1))()
+        _check(self.lib.ob_cltk_layout(self._ctx, out), "ob_cltk_layout")
+        self.K = K.value
+        return list(out)
+
+    def cltk_step(self, step, grads, memory, index, values, average, stream=None) -> None:
+        """One cyclic-local-top-k exchange (see include/ob.h)."""
+        f32 = (torch.float32,)
+        st = self.lib.ob_cltk_step(
+            self._ctx, int(step), self._grad_ptr(grads), _ptr(memory, f32, self.W * self.N, "memory"),
+            _ptr(index, (torch.int32,), self.K, "index"), _ptr(values, f32, self.W * self.K, "values"),
+            _ptr(average, f32, self.K, "average"), _stream(stream))
+        _check(st, "ob_cltk_step")
 
     def set_server_chunks(self, chunks: int) -> None:
         """Partition the server C ways (one scale per tensor chunk); see include/ob.h."""

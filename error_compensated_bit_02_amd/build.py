@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libob.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "topk.hip"),
+           os.path.join(CSRC, "api.cpp")]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -38,6 +38,10 @@ struct ob_ctx {
   bool trust_ratio = false;          // layer-wise trust-ratio update
   float weight_decay = 0.0f;
   float *d_ratio = nullptr;          // [T] trust ratios (device scratch)
+  // cyclic local top-k codec (allocated by ob_cltk_configure)
+  void *topk_scratch = nullptr;
+  ob::TopkArgs topk{};
+  std::vector<int64_t> k_off;        // host copy [T+1]
   int32_t *d_tile_piece = nullptr;   // device views into scratch
   int32_t *d_piece_begin = nullptr;
   int64_t *d_piece_numel = nullptr;
@@ -55,7 +59,7 @@ const char *const kKindNames[ob::K_NUM_KINDS] = {
     "worker_pass1", "scale_finalize", "worker_pass2", "server_pass1",
     "server_pass2", "server_pass2_update", "apply_update", "worker_residual",
     "server_residual", "update_residual", "materialize", "warmup", "zero_errors",
-    "trust_norms", "trust_ratio"};
+    "trust_norms", "trust_ratio", "cltk_step"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -353,6 +357,7 @@ void ob_destroy(ob_ctx *c) {
     if (e.stop) (void)hipEventDestroy(e.stop);
   }
   if (c->scratch) (void)hipFree(c->scratch);
+  if (c->topk_scratch) (void)hipFree(c->topk_scratch);
   delete c;
 }
 
@@ -496,6 +501,81 @@ int ob_set_trust_ratio(ob_ctx *c, int32_t enable, double weight_decay) {
   c->trust_ratio = enable != 0;
   c->weight_decay = static_cast<float>(weight_decay);
   return OB_OK;
+}
+
+int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
+  if (c == nullptr || !std::isfinite(density) || density <= 0.0 || density > 1.0)
+    return OB_ERR_INVALID;
+  for (int32_t t = 0; t < c->T; ++t)   // index entries are int32 positions within a tensor
+    if (c->numel[t] > INT32_MAX) return OB_ERR_INVALID;
+  if (hipDeviceSynchronize() != hipSuccess) return OB_ERR_DEVICE;   // old tables may be in use
+  std::vector<int64_t> k_off(static_cast<size_t>(c->T) + 1, 0);
+  for (int32_t t = 0; t < c->T; ++t) {
+    const int64_t k = std::max<int64_t>(1, static_cast<int64_t>(std::ceil(density * static_cast<double>(c->numel[t]))));
+    k_off[t + 1] = k_off[t] + std::min(k, c->numel[t]);
+  }
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t T = static_cast<size_t>(c->T), tiles = static_cast<size_t>(c->num_tiles);
+  const size_t nw = static_cast<size_t>(c->N / 64);
+  const size_t sizes[] = {up((T + 1) * 8), up(T * 256 * 4), up(T * 4), up(T * 4), up(tiles * 4),
+                          up(tiles * 4), up(tiles * 8), up(tiles * 8), up(nw * 8), up(nw * 8)};
+  size_t total = 0;
+  for (size_t b : sizes) total += b;
+  if (c->topk_scratch) {
+    (void)hipFree(c->topk_scratch);
+    c->topk_scratch = nullptr;
+  }
+  if (hipMalloc(&c->topk_scratch, total) != hipSuccess) {
+    (void)hipGetLastError();
+    return OB_ERR_NOMEM;
+  }
+  unsigned char *p = static_cast<unsigned char *>(c->topk_scratch);
+  ob::TopkArgs &a = c->topk;
+  a = ob::TopkArgs{};
+  unsigned char *at[10];
+  for (int i = 0; i < 10; ++i) {
+    at[i] = p;
+    p += sizes[i];
+  }
+  a.k_off = reinterpret_cast<const int64_t *>(at[0]);
+  a.hist = reinterpret_cast<uint32_t *>(at[1]);
+  a.prefix = reinterpret_cast<uint32_t *>(at[2]);
+  a.krem = reinterpret_cast<uint32_t *>(at[3]);
+  a.tile_gt = reinterpret_cast<uint32_t *>(at[4]);
+  a.tile_eq = reinterpret_cast<uint32_t *>(at[5]);
+  a.tile_eq_before = reinterpret_cast<int64_t *>(at[6]);
+  a.tile_sel_off = reinterpret_cast<int64_t *>(at[7]);
+  a.sel_words = reinterpret_cast<uint64_t *>(at[8]);
+  a.word_pos = reinterpret_cast<int64_t *>(at[9]);
+  a.K = k_off[T];
+  if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess)
+    return OB_ERR_DEVICE;
+  c->k_off = k_off;
+  if (k_total) *k_total = a.K;
+  return OB_OK;
+}
+
+int ob_cltk_layout(const ob_ctx *c, int64_t *k_off) {
+  if (c == nullptr || k_off == nullptr || c->topk_scratch == nullptr) return OB_ERR_INVALID;
+  std::copy(c->k_off.begin(), c->k_off.end(), k_off);
+  return OB_OK;
+}
+
+int ob_cltk_step(ob_ctx *c, int64_t step, const void *grads, float *memory, int32_t *index,
+                 float *values, float *average, void *stream) {
+  if (c == nullptr || c->topk_scratch == nullptr || step < 0) return OB_ERR_INVALID;
+  const int st = check_ptrs(grads, memory, index, values, average);
+  if (st) return st;
+  ob::TopkArgs a = c->topk;
+  a.grads = grads;
+  a.memory = memory;
+  a.index = index;
+  a.values = values;
+  a.average = average;
+  a.leader = static_cast<int>(step % c->W);
+  a.wgroup = ob::worker_group_size(c->W, c->num_tiles);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return timed(c, ob::K_TOPK, s, [&] { ob::launch_topk(c->geo, c->bf16, a, s); });
 }
 
 int ob_profile_enable(ob_ctx *c, int32_t enable) {

@@ -73,6 +73,7 @@ enum Kind {
   K_ZERO_ERRORS,
   K_TRUST_NORMS,
   K_TRUST_RATIO,
+  K_TOPK,
   K_NUM_KINDS
 };
 
@@ -147,6 +148,30 @@ struct WarmupArgs {
   float *params;             // [N]
   float c1, c2, b2, cb2, lr, eps;
 };
+
+// Cyclic local top-k codec (topk.hip).
+struct TopkArgs {
+  const void *grads;         // [W][N] fp32 or bf16
+  float *memory;             // [W][N] local memories, read and overwritten
+  int32_t *index;            // [K] positions within each tensor, ascending per tensor
+  float *values;             // [W][K] messages
+  float *average;            // [K] the server's average
+  int64_t K;                 // total entries over the tensor list
+  const int64_t *k_off;      // [T+1] tensor t's entries are k_off[t] .. k_off[t+1]-1
+  uint32_t *hist;            // [T][256] radix histograms
+  uint32_t *prefix;          // [T] key prefix found so far, then the k-th largest key
+  uint32_t *krem;            // [T] rank still to find, then the ties to take
+  uint32_t *tile_gt;         // [num_tiles] keys above the threshold
+  uint32_t *tile_eq;         // [num_tiles] keys at the threshold
+  int64_t *tile_eq_before;   // [num_tiles] keys at the threshold in earlier tiles of the tensor
+  int64_t *tile_sel_off;     // [num_tiles] position of the tile's first selected entry
+  uint64_t *sel_words;       // [Nw] selection bitmask (bit l of word j: element 64 j + l)
+  int64_t *word_pos;         // [Nw] position of each word's first selected entry
+  int leader;                // worker whose values rank the positions
+  int wgroup;                // workers per workgroup in the gather pass
+};
+
+void launch_topk(const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s);
 
 void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s);
 // Scales of rows [row0, row0 + nrows) of the partials over `count` items

@@ -207,6 +207,31 @@ int32_t ob_server_scale_count(const ob_ctx *ctx);
  * more read of v and params.  weight_decay >= 0 and finite. */
 int ob_set_trust_ratio(ob_ctx *ctx, int32_t enable, double weight_decay);
 
+/* Cyclic local top-k (CLT-k), an alternative codec for the exchange: the
+ * commutative compressor of the review of "ScaleCom: Scalable Sparsified
+ * Gradient Compression for Communication-Efficient Distributed Training"
+ * (Proposed method, bullet 1; Main results, bullet 3).  Per tensor t with
+ * k_t = max(1, ceil(density * n_t)) entries kept:
+ *   x_w     = memory_w + g_w                              (fp32, every worker)
+ *   index   = the k_t positions of largest |x_leader|, leader = step mod W,
+ *             ties to the lower position, listed in ascending order
+ *   values_w = x_w at index;  memory_w = x_w with those positions set to 0
+ *   average = (sum over w ascending, from +0, of values_w) / W
+ * The page names a low-pass filter on the memory without its form; none is
+ * applied.  Inputs must be finite.
+ *
+ * ob_cltk_configure allocates the codec's scratch for the given density
+ * (0 < density <= 1; every n_t at most INT32_MAX, else OB_ERR_INVALID;
+ * synchronous) and returns K = sum of k_t; ob_cltk_layout writes the host
+ * array k_off[0..T] (tensor t's entries are k_off[t] .. k_off[t+1]-1).
+ * ob_cltk_step: grads [W][N] read; memory [W][N] fp32 read and overwritten;
+ * index [K] int32 (position within the tensor), values [W][K] fp32 and
+ * average [K] fp32 written. */
+int ob_cltk_configure(ob_ctx *ctx, double density, int64_t *k_total);
+int ob_cltk_layout(const ob_ctx *ctx, int64_t *k_off);
+int ob_cltk_step(ob_ctx *ctx, int64_t step, const void *grads, float *memory, int32_t *index,
+                 float *values, float *average, void *stream);
+
 /* Kernel timing for measurement.  With profiling on, every kernel the context
  * launches is bracketed by HIP events on its stream.  ob_profile_read waits for
  * the recorded events, writes per kernel kind the summed milliseconds and the

@@ -60,6 +60,16 @@ The pages give no formulas.  The readings taken where they are silent:
       weight decay wd > 0 is given) as in R8; per tensor the trust ratio
       r = fp32(sqrt64(fl64(sum p^2)) / sqrt64(fl64(sum u^2))), r = 1 when either
       sum is 0; p <- p - lr*(r*u).
+  R15 cyclic local top-k (the review of "ScaleCom", Proposed method: a
+      commutative compressor, cyclic local top-k, that aligns the workers'
+      sparsity; an alternative codec for the exchange): at step t the leader
+      is worker t mod W; per tensor, x_w = mem_w + g_w (fp32); the index set
+      is the k positions of largest |x_leader| (ties to the lower index),
+      listed in ascending order; every worker sends its x_w at those
+      positions; its memory becomes x_w with those positions set to 0 (plain
+      error feedback: the page names a low-pass filter on the memory without
+      its form, so none is applied); the server averages the W messages as in
+      R6.  k = max(1, ceil(density * n)).
 
 All floating point below is numpy float32 (IEEE binary32, round to nearest
 even; numpy never contracts a*b+c) except the scale, which is fp64 as R1 says.
@@ -357,6 +367,35 @@ def warmup_step(st: TensorState, grads: np.ndarray, beta1: float, beta2: float,
     v = F32(beta2) * st.v + F32(1.0 - float(beta2)) * (gbar * gbar)
     p = preconditioned_update(st.p, m, v, lr, eps)
     return TensorState(p, m, v, st.err_s.copy(), st.err_w.copy())
+
+
+@dataclass
+class TopKResult:
+    index: np.ndarray    # int64 [k] ascending positions within the tensor
+    values: np.ndarray   # fp32 [W][k] each worker's message
+    average: np.ndarray  # fp32 [k] the server's average
+    memory: np.ndarray   # fp32 [W][n] the workers' new memories
+
+
+def cltk_k(n: int, density: float) -> int:
+    """Entries kept per tensor (R15)."""
+    return max(1, int(np.ceil(density * n)))
+
+
+def cltk_step(memory: np.ndarray, grads: np.ndarray, step: int, k: int) -> TopKResult:
+    """One cyclic-local-top-k exchange of one tensor (R15)."""
+    W, n = memory.shape
+    x = np.stack([memory[w] + widen_grad(grads[w]) for w in range(W)])
+    lead = np.abs(x[step % W]).astype(np.float64)
+    order = np.lexsort((np.arange(n), -lead))          # |x| descending, index ascending
+    index = np.sort(order[:k])
+    values = x[:, index]
+    mem = x.copy()
+    mem[:, index] = F32(0.0)
+    acc = np.zeros(k, dtype=np.float32)
+    for w in range(W):
+        acc = acc + values[w]
+    return TopKResult(index, values, acc / F32(W), mem)
 
 
 def message_bytes(n: int) -> int:

@@ -509,4 +509,51 @@ def pin_trust_ratio_update():
                           ob.preconditioned_update(ones, m1, v1, 0.1, 0.0))
 
 
+def pin_cltk_brute_force():
+    """Top-k positions by a pure-Python sort of (|x|, -index), ties included."""
+    rng = _rng(21)
+    for trial in range(30):
+        W, n = int(rng.integers(1, 5)), int(rng.integers(1, 80))
+        mem = rng.choice(np.array([-2, -1, -0.0, 0, 1, 2, 3], np.float32), (W, n))
+        g = rng.choice(np.array([-1, 0, 1, 0.5], np.float32), (W, n))
+        k = int(rng.integers(1, n + 1))
+        step = int(rng.integers(0, 10))
+        out = ob.cltk_step(mem, g, step, k)
+        x = [[float(np.float32(mem[w][i] + g[w][i])) for i in range(n)] for w in range(W)]
+        lead = x[step % W]
+        ranked = sorted(range(n), key=lambda i: (-abs(lead[i]), i))
+        assert out.index.tolist() == sorted(ranked[:k]), trial
+        for w in range(W):
+            assert out.values[w].tolist() == [x[w][i] for i in sorted(ranked[:k])]
+            kept = set(ranked[:k])
+            assert out.memory[w].tolist() == [0.0 if i in kept else x[w][i] for i in range(n)]
+
+
+def pin_cltk_commutative():
+    """The page's claim: with one index set for all workers, the average of
+    the compressed messages is the compression of the average (same positions),
+    so the exchange is an all-reduce; and memory + message = x exactly."""
+    rng = _rng(22)
+    W, n, k = 4, 3000, 40
+    mem = (rng.standard_normal((W, n)) * 1e-3).astype(np.float32)
+    g = (rng.standard_normal((W, n)) * 1e-3).astype(np.float32)
+    for step in range(W + 1):
+        out = ob.cltk_step(mem, g, step, k)
+        x = mem + g
+        dense_avg = np.zeros(n, np.float32)
+        for w in range(W):
+            dense_avg = dense_avg + x[w]
+        dense_avg = dense_avg / np.float32(W)
+        assert np.array_equal(out.average, dense_avg[out.index])
+        for w in range(W):
+            back = out.memory[w].copy()
+            back[out.index] = out.values[w]
+            assert np.array_equal(back, x[w])
+        # the leader's kept entries dominate its dropped ones
+        lead = np.abs(x[step % W])
+        dropped = np.delete(lead, out.index)
+        assert lead[out.index].min() >= (dropped.max() if dropped.size else 0)
+    assert ob.cltk_k(100, 0.01) == 1 and ob.cltk_k(1000, 0.01) == 10 and ob.cltk_k(5, 0.01) == 1
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,113 @@
+"""Cyclic local top-k codec (ob_cltk_step) against the oracle's cltk_step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.onebit as ob
+from harness import log
+from synth import WORKLOADS, grads_for_step, host_slice, init_state
+from synth.workloads import Workload, padded_layout
+from test_parity_gpu import RAGGED, _wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from error_compensated_bit_02_amd import load_library
+    load_library()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _run(wl: Workload, density: float, steps: int, tensors=None, grads_fn=None, memory=None):
+    from error_compensated_bit_02_amd import OneBitAdam
+    ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
+    k_off = ctx.cltk_configure(density)
+    off, N = padded_layout(wl.numel)
+    tensors = list(range(wl.num_tensors)) if tensors is None else tensors
+    for t in range(wl.num_tensors):
+        assert k_off[t + 1] - k_off[t] == min(ob.cltk_k(wl.numel[t], density), wl.numel[t])
+    mem = init_state(wl, "cuda")["err_w"] if memory is None else memory
+    if memory is None:
+        mem.normal_(0.0, 1e-3)
+        for t, n in enumerate(wl.numel):
+            mem[:, off[t] + n: off[t + 1]] = 0.0
+    K = ctx.K
+    index = torch.zeros(K, dtype=torch.int32, device="cuda")
+    values = torch.zeros(wl.workers, K, dtype=torch.float32, device="cuda")
+    average = torch.zeros(K, dtype=torch.float32, device="cuda")
+    ref_mem = [host_slice(mem, off[t], off[t] + wl.numel[t]) for t in tensors]
+    exact = total = 0
+    for k in range(steps):
+        g = grads_for_step(wl, k, "cuda") if grads_fn is None else grads_fn(k)
+        host_g = [host_slice(g, off[t], off[t] + wl.numel[t]) for t in tensors]
+        ctx.cltk_step(k, g, mem, index, values, average)
+        torch.cuda.synchronize()
+        for i, t in enumerate(tensors):
+            kt = ob.cltk_k(wl.numel[t], density)
+            out = ob.cltk_step(ref_mem[i], host_g[i], k, kt)
+            lo, hi = k_off[t], k_off[t + 1]
+            got_idx = index[lo:hi].cpu().numpy()
+            assert np.array_equal(got_idx, out.index), f"step {k} tensor {t}: index differs"
+            got_vals = values[:, lo:hi].cpu().numpy()
+            assert np.array_equal(got_vals.view(np.uint32), out.values.view(np.uint32)), (k, t)
+            got_avg = average[lo:hi].cpu().numpy()
+            assert np.array_equal(got_avg.view(np.uint32), out.average.view(np.uint32)), (k, t)
+            got_mem = host_slice(mem, off[t], off[t] + wl.numel[t])
+            assert np.array_equal(got_mem.view(np.uint32), out.memory.view(np.uint32)), (k, t)
+            ref_mem[i] = out.memory
+            exact += got_idx.size + got_vals.size + got_avg.size + got_mem.size
+            total += got_idx.size + got_vals.size + got_avg.size + got_mem.size
+        log(f"  {wl.name} cltk step {k}: ok")
+    ctx.close()
+    return exact, total
+
+
+@pytest.mark.parametrize("W,density", [(3, 0.01), (4, 0.1), (1, 0.5), (8, 1.0)])
+def test_cltk_ragged(W, density):
+    wl = _wl(f"cltk_w{W}", RAGGED, W, steps=4)
+    exact, total = _run(wl, density, wl.steps)
+    log(f"cltk W={W} density={density}: {exact}/{total} values bit-identical")
+
+
+def test_cltk_ties_and_zeros():
+    """Many equal magnitudes (ties broken by position) and zero memories."""
+    wl = _wl("cltk_ties_w2", (5000, 64, 130), 2, steps=3)
+    off, _ = padded_layout(wl.numel)
+
+    def grads_fn(k):
+        g = grads_for_step(wl, k, "cuda")
+        g.copy_(torch.round(g * 1024.0) / 1024.0)   # few distinct magnitudes -> many ties
+        for t, n in enumerate(wl.numel):
+            g[:, off[t] + n: off[t + 1]] = 0.0
+        return g
+    memory = torch.zeros(wl.workers, padded_layout(wl.numel)[1], device="cuda")
+    exact, total = _run(wl, 0.05, wl.steps, grads_fn=grads_fn, memory=memory)
+    log(f"cltk ties: {exact}/{total}")
+
+
+def test_cltk_configure_rejects_bad_density():
+    from error_compensated_bit_02_amd import OneBitAdam, OneBitError
+    ctx = OneBitAdam((100, 7), 2, "f32", 0.9, 1e-8)
+    for bad in (0.0, -0.1, 1.5, float("nan")):
+        with pytest.raises(OneBitError):
+            ctx.cltk_configure(bad)
+    assert ctx.cltk_configure(1.0) == [0, 100, 107]
+    assert ctx.cltk_configure(0.001) == [0, 1, 2]
+    ctx.close()
+
+
+def test_cltk_bf16():
+    wl = _wl("cltk_bf16_w8", RAGGED, 8, dtype="bf16", steps=3, g_sigma=5e-4)
+    _run(wl, 0.02, wl.steps)
+
+
+def test_cltk_full_size_bert_large_sampled():
+    wl = WORKLOADS["bert_large"]
+    idx = {n: i for i, (n, _) in enumerate(wl.tensors)}
+    tensors = [idx[n] for n in ("layer0.attn.q.bias", "layer3.attn.v.weight", "embed.position")]
+    _run(wl, 0.01, 3, tensors=tensors)

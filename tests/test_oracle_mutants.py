@@ -125,6 +125,30 @@ MUTANTS["trust_ratio_squared_norms"] = ("trust_ratio", lambda p, u: F32(1.0) if 
     ob.sum_of_squares(p) / ob.sum_of_squares(u)))
 
 
+def _cltk_mutant(kind):
+    orig = ob.cltk_step
+
+    def cltk_step(memory, grads, step, k):
+        if kind == "leader":
+            return orig(memory, grads, step + 1, k)
+        out = orig(memory, grads, step, k)
+        if kind == "memory_keeps_sent":
+            out.memory = np.stack([memory[w] + ob.widen_grad(grads[w]) for w in range(memory.shape[0])])
+        if kind == "ties_high_index":
+            W, n = memory.shape
+            x = np.stack([memory[w] + ob.widen_grad(grads[w]) for w in range(W)])
+            lead = np.abs(x[step % W]).astype(np.float64)
+            order = np.lexsort((-np.arange(n), -lead))
+            out.index = np.sort(order[:k])
+        return out
+    return cltk_step
+
+
+MUTANTS["cltk_wrong_leader"] = ("cltk_step", _cltk_mutant("leader"))
+MUTANTS["cltk_memory_keeps_sent"] = ("cltk_step", _cltk_mutant("memory_keeps_sent"))
+MUTANTS["cltk_ties_to_high_index"] = ("cltk_step", _cltk_mutant("ties_high_index"))
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
