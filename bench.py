@@ -65,6 +65,17 @@ def kernel_bytes_per_element(wl) -> dict:
     }
 
 
+def cltk_bytes_per_element(wl, density: float) -> dict:
+    """Bytes per element each stage of the cyclic local top-k exchange must
+    move, its own operands touched once (density d = kept fraction)."""
+    W, g, d = wl.workers, grad_bytes(wl), density
+    return {
+        "cltk_select": g + 4.0 + 4.0 * d,          # read the leader's memory and gradient; write index
+        "cltk_gather": (g + 8.0) * W + 4.0 * d * W,  # read memory and gradient, write memory; write values
+        "cltk_average": d * (4.0 * W + 4.0),       # read values, write the average
+    }
+
+
 def counter_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
@@ -151,6 +162,56 @@ def time_form(form, wl, ctx, grads, steps, warmup, stream):
     return dt, kernels, st
 
 
+def time_cltk(wl, ctx, grads, density, steps, warmup, stream):
+    """Warmup, then `steps` timed exchanges of the cyclic local top-k codec
+    (the leader cycles with the step).  Returns (seconds, kernels)."""
+    import torch
+    from synth.workloads import padded_layout
+    ctx.cltk_configure(density)
+    _, N = padded_layout(wl.numel)
+    memory = torch.zeros(wl.workers, N, dtype=torch.float32, device="cuda")
+    index = torch.empty(ctx.K, dtype=torch.int32, device="cuda")
+    values = torch.empty(wl.workers, ctx.K, dtype=torch.float32, device="cuda")
+    average = torch.empty(ctx.K, dtype=torch.float32, device="cuda")
+    sets = len(grads)
+    for k in range(warmup):
+        ctx.cltk_step(k, grads[k % sets], memory, index, values, average, stream=stream)
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    ctx.profile_read(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ctx.cltk_step(warmup + k, grads[(warmup + k) % sets], memory, index, values, average,
+                      stream=stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kernels = ctx.profile_read(reset=True)
+    ctx.profile(False)
+    del memory, index, values, average
+    return dt, kernels
+
+
+def summarize_cltk(wl, n_elem, steps, dt, kernels, density, workload):
+    kb = cltk_bytes_per_element(wl, density)
+    per = {k: (kernels[k][0] / kernels[k][1] if kernels[k][1] else 0.0) for k in kb}
+    dom = max(kb, key=lambda k: per[k])
+    achieved = kb[dom] * n_elem / (per[dom] * 1e-3) / 1e9
+    ms = dt * 1e3 / steps
+    total = sum(kb.values())
+    traffic = counter_traffic(workload, dom)
+    return {
+        "density": density, "ms_per_exchange": ms, "elements_per_s": n_elem * steps / dt,
+        "exchange_hbm_gbps_algorithmic": round(total * n_elem / (ms * 1e-3) / 1e9, 1),
+        "exchange_bytes_per_element": total,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "bytes_per_element": kb[dom], "avg_ms": round(per[dom], 4)},
+        "kernels": {k: {"avg_ms": round(per[k], 4), "launches": kernels[k][1]} for k in kb},
+    }
+
+
 def summarize(wl, n_elem, steps, dt, kernels, workload):
     ms_step = dt * 1e3 / steps
     b_alg = step_bytes_per_element(wl)
@@ -191,6 +252,9 @@ def main() -> int:
                     help="layer-wise trust-ratio update with weight decay WD")
     ap.add_argument("--server-chunks", type=int, default=1,
                     help="partitioned server: one server scale per tensor chunk (1 = per tensor)")
+    ap.add_argument("--cltk-density", type=float, default=0.01,
+                    help="also time the cyclic local top-k exchange keeping this fraction of "
+                         "each tensor (0 = skip)")
     ap.add_argument("--cpu-sample-tensors", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -244,6 +308,14 @@ def main() -> int:
         log(f"bench: {form}: {results[form]['ms_per_step']:.3f} ms/step, "
             f"{100 * results[form]['step_frac_of_peak']:.1f}% of peak")
 
+    cltk = None
+    if args.cltk_density > 0:
+        torch.cuda.empty_cache()
+        dt, kernels = time_cltk(wl, ctx, grads, args.cltk_density, args.steps, args.warmup, stream)
+        cltk = summarize_cltk(wl, n_elem, args.steps, dt, kernels, args.cltk_density, wl.name)
+        log(f"bench: cltk density {args.cltk_density}: {cltk['ms_per_exchange']:.3f} ms/exchange, "
+            f"{cltk['roofline']['kernel']} at {100 * cltk['roofline']['frac']:.1f}% of peak")
+
     head = results[forms[0]]
     result = {
         "metric": METRIC, "value": head["value"], "unit": "elements/s", "n_gpus": 1,
@@ -263,6 +335,7 @@ def main() -> int:
     }
     if "strict" in results and forms[0] != "strict":
         result["strict_form"] = results["strict"]
+    result["cltk"] = cltk
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (cpu baseline)")

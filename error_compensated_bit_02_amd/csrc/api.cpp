@@ -55,11 +55,13 @@ struct ob_ctx {
 
 namespace {
 
-const char *const kKindNames[ob::K_NUM_KINDS] = {
+const char *const kKindNames[] = {
     "worker_pass1", "scale_finalize", "worker_pass2", "server_pass1",
     "server_pass2", "server_pass2_update", "apply_update", "worker_residual",
     "server_residual", "update_residual", "materialize", "warmup", "zero_errors",
-    "trust_norms", "trust_ratio", "cltk_step"};
+    "trust_norms", "trust_ratio", "cltk_select", "cltk_gather", "cltk_average"};
+static_assert(sizeof(kKindNames) / sizeof(kKindNames[0]) == ob::K_NUM_KINDS,
+              "one name per kernel kind");
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -517,8 +519,9 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t T = static_cast<size_t>(c->T), tiles = static_cast<size_t>(c->num_tiles);
   const size_t nw = static_cast<size_t>(c->N / 64);
-  const size_t sizes[] = {up((T + 1) * 8), up(T * 256 * 4), up(T * 4), up(T * 4), up(tiles * 4),
-                          up(tiles * 4), up(tiles * 8), up(tiles * 8), up(nw * 8), up(nw * 8)};
+  const size_t sizes[] = {up((T + 1) * 8), up(T * 2048 * 4), up(T * 4),  up(T * 4),
+                          up(tiles * 4),     up(tiles * 4),    up(tiles * 8), up(tiles * 8),
+                          up(nw * 8),        up(nw * 8),       up(nw * 64 * 4)};
   size_t total = 0;
   for (size_t b : sizes) total += b;
   if (c->topk_scratch) {
@@ -532,8 +535,9 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   unsigned char *p = static_cast<unsigned char *>(c->topk_scratch);
   ob::TopkArgs &a = c->topk;
   a = ob::TopkArgs{};
-  unsigned char *at[10];
-  for (int i = 0; i < 10; ++i) {
+  constexpr int kSections = sizeof(sizes) / sizeof(sizes[0]);
+  unsigned char *at[kSections];
+  for (int i = 0; i < kSections; ++i) {
     at[i] = p;
     p += sizes[i];
   }
@@ -547,6 +551,7 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   a.tile_sel_off = reinterpret_cast<int64_t *>(at[7]);
   a.sel_words = reinterpret_cast<uint64_t *>(at[8]);
   a.word_pos = reinterpret_cast<int64_t *>(at[9]);
+  a.keys = reinterpret_cast<uint32_t *>(at[10]);
   a.K = k_off[T];
   if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess)
     return OB_ERR_DEVICE;
@@ -575,7 +580,15 @@ int ob_cltk_step(ob_ctx *c, int64_t step, const void *grads, float *memory, int3
   a.leader = static_cast<int>(step % c->W);
   a.wgroup = ob::worker_group_size(c->W, c->num_tiles);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return timed(c, ob::K_TOPK, s, [&] { ob::launch_topk(c->geo, c->bf16, a, s); });
+  int st2 = timed(c, ob::K_TOPK_SELECT, s,
+                  [&] { ob::launch_topk(ob::TopkStage::kSelect, c->geo, c->bf16, a, s); });
+  if (st2 == OB_OK)
+    st2 = timed(c, ob::K_TOPK_GATHER, s,
+                [&] { ob::launch_topk(ob::TopkStage::kGather, c->geo, c->bf16, a, s); });
+  if (st2 == OB_OK)
+    st2 = timed(c, ob::K_TOPK_AVERAGE, s,
+                [&] { ob::launch_topk(ob::TopkStage::kAverage, c->geo, c->bf16, a, s); });
+  return st2;
 }
 
 int ob_profile_enable(ob_ctx *c, int32_t enable) {

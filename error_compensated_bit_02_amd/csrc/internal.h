@@ -73,7 +73,9 @@ enum Kind {
   K_ZERO_ERRORS,
   K_TRUST_NORMS,
   K_TRUST_RATIO,
-  K_TOPK,
+  K_TOPK_SELECT,
+  K_TOPK_GATHER,
+  K_TOPK_AVERAGE,
   K_NUM_KINDS
 };
 
@@ -158,7 +160,8 @@ struct TopkArgs {
   float *average;            // [K] the server's average
   int64_t K;                 // total entries over the tensor list
   const int64_t *k_off;      // [T+1] tensor t's entries are k_off[t] .. k_off[t+1]-1
-  uint32_t *hist;            // [T][256] radix histograms
+  uint32_t *keys;            // [N] the leader's keys, bit patterns of |memory + grads|
+  uint32_t *hist;            // [T][2048] radix histograms
   uint32_t *prefix;          // [T] key prefix found so far, then the k-th largest key
   uint32_t *krem;            // [T] rank still to find, then the ties to take
   uint32_t *tile_gt;         // [num_tiles] keys above the threshold
@@ -171,7 +174,11 @@ struct TopkArgs {
   int wgroup;                // workers per workgroup in the gather pass
 };
 
-void launch_topk(const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s);
+// The codec's three stages: the leader's selection (radix select, offsets,
+// index list), the gather of every worker's message with the memory update,
+// and the server's average.
+enum class TopkStage { kSelect, kGather, kAverage };
+void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s);
 
 void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s);
 // Scales of rows [row0, row0 + nrows) of the partials over `count` items

@@ -6,8 +6,10 @@
 // Per tensor, the leader worker (step mod W) ranks |x_leader| = |mem + g|
 // and every worker sends its x at the leader's k largest positions.  The
 // selection is exact: the k-th largest key (the bit pattern of |x|, which
-// orders non-negative floats) is found by a 4-pass radix select with 8-bit
-// digits (per-tile LDS histograms added into per-tensor histograms), ties at
+// orders non-negative floats) is found by a 3-pass radix select with 11, 11
+// and 9-bit digits (per-tile LDS histograms added into per-tensor
+// histograms); the first pass also stores the keys, so the later passes read
+// 4 bytes per element instead of the leader's memory and gradient.  Ties at
 // that key go to the lowest indices, and the positions are written in
 // ascending order through per-tile offsets.  Then one dense pass over all
 // workers gathers the messages and updates the memories, and the server
@@ -16,7 +18,10 @@
 // The element mapping is the one of kernels.hip: a workgroup of 4
 // wavefronts owns a tile of up to kTile elements of one tensor, lane l of
 // wavefront v owns element 2048 v + 64 c + l, so ballots over one c are
-// natural-order 64-bit words.
+// natural-order 64-bit words.  Every per-tile kernel has a body for full
+// tiles (no bounds tests: loads from one base address with immediate
+// offsets, all issued before the first use) and one for a tensor's last,
+// partial tile (guarded loads).
 #include "internal.h"
 
 #pragma clang fp contract(off)
@@ -49,16 +54,23 @@ __device__ __forceinline__ TileLanes tile_lanes(const Tile &tl) {
   return r;
 }
 
-__device__ __forceinline__ bool valid(const Tile &tl, const TileLanes &ln, int c) {
-  return ln.sub0 + 64 * c + ln.lane < tl.len;
+// Whether lane slot c holds an element of the tile.
+template <bool kFull>
+__device__ __forceinline__ bool slot_ok(const Tile &tl, const TileLanes &ln, int c) {
+  return kFull || ln.sub0 + 64 * c + ln.lane < tl.len;
 }
 
-// Ranking key of the leader's element: the bit pattern of |mem + g|.
+// Ranking key of an element: the bit pattern of |mem + g|.
 template <typename G>
-__device__ __forceinline__ uint32_t leader_key(const TopkArgs &a, const Geometry &g, int64_t i) {
-  const size_t off = static_cast<size_t>(a.leader) * g.N + i;
-  const float x = a.memory[off] + grad_at(static_cast<const G *>(a.grads) + off);
-  return __float_as_uint(x) & 0x7fffffffu;
+__device__ __forceinline__ uint32_t key_of(const float *mem, const G *grads, int64_t i) {
+  return __float_as_uint(mem[i] + grad_at(grads + i)) & 0x7fffffffu;
+}
+
+// Lane c's value of a 64-bit register, as a wave-uniform (scalar) value.
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int c) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), c);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), c);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
@@ -66,86 +78,156 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// radix select
+// radix select over the 31-bit keys: digits of 11, 11 and 9 bits
 // ---------------------------------------------------------------------------
+constexpr int kMaxBins = 2048;
+constexpr int kShift0 = 20, kShift1 = 9, kShift2 = 0;
+
 __global__ __launch_bounds__(kBlock) void topk_reset(Geometry g, TopkArgs a) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (i < static_cast<int64_t>(g.T) * 256) a.hist[i] = 0u;
+  if (i < static_cast<int64_t>(g.T) * kMaxBins) a.hist[i] = 0u;
   if (i < g.T) {
     a.prefix[i] = 0u;
     a.krem[i] = static_cast<uint32_t>(a.k_off[i + 1] - a.k_off[i]);
   }
 }
 
-// Histogram of digit (key >> shift) & 255 over the keys whose higher digits
-// equal the tensor's prefix so far.
-template <typename G>
-__global__ __launch_bounds__(kBlock) void topk_hist(Geometry g, TopkArgs a, int shift) {
-  __shared__ uint32_t h[256];
-  h[threadIdx.x] = 0u;
+template <typename G, bool kFirst, bool kFull>
+__device__ __forceinline__ void hist_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
+                                          uint32_t *h, int shift, int nb, uint32_t hi_mask,
+                                          uint32_t want) {
+  const TileLanes ln = tile_lanes(tl);
+  const size_t row = static_cast<size_t>(a.leader) * g.N + ln.base + ln.lane;
+  const float *mem = a.memory + row;
+  const G *grads = static_cast<const G *>(a.grads) + row;
+  const uint32_t *keys_in = a.keys + ln.base + ln.lane;
+  uint32_t key[kPerLane];
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {   // all loads first
+    key[c] = 0u;
+    if (slot_ok<kFull>(tl, ln, c)) key[c] = kFirst ? key_of(mem, grads, 64 * c) : keys_in[64 * c];
+  }
+  uint32_t *keys_out = a.keys + ln.base + ln.lane;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    if (!slot_ok<kFull>(tl, ln, c)) continue;
+    if (kFirst) keys_out[64 * c] = key[c];
+    if ((key[c] & hi_mask) == want) atomicAdd(&h[(key[c] >> shift) & (nb - 1)], 1u);
+  }
+}
+
+// Histogram of digit (key >> shift) & (2^bits - 1) over the keys whose higher
+// digits equal the tensor's prefix so far.  The first pass (kFirst) computes
+// the keys from the leader's memory and gradient and stores them.
+template <typename G, bool kFirst>
+__global__ __launch_bounds__(kBlock) void topk_hist(Geometry g, TopkArgs a, int shift, int bits) {
+  __shared__ uint32_t h[kMaxBins];
+  const int nb = 1 << bits;
+  for (int i = threadIdx.x; i < nb; i += kBlock) h[i] = 0u;
   __syncthreads();
   const Tile tl = g.tiles[blockIdx.x];
-  const TileLanes ln = tile_lanes(tl);
-  const uint32_t hi_mask = shift >= 24 ? 0u : ~((1u << (shift + 8)) - 1u);
+  const uint32_t hi_mask = shift + bits >= 31 ? 0u : ~((1u << (shift + bits)) - 1u);
   const uint32_t want = a.prefix[tl.tensor] & hi_mask;
-  for (int c = 0; c < kPerLane; ++c) {
-    if (!valid(tl, ln, c)) continue;
-    const uint32_t key = leader_key<G>(a, g, ln.base + 64 * c + ln.lane);
-    if ((key & hi_mask) == want) atomicAdd(&h[(key >> shift) & 255u], 1u);
-  }
+  if (tl.len == kTile)
+    hist_tile<G, kFirst, true>(g, a, tl, h, shift, nb, hi_mask, want);
+  else
+    hist_tile<G, kFirst, false>(g, a, tl, h, shift, nb, hi_mask, want);
   __syncthreads();
-  const uint32_t n = h[threadIdx.x];
-  if (n) atomicAdd(&a.hist[static_cast<size_t>(tl.tensor) * 256 + threadIdx.x], n);
+  uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
+  for (int i = threadIdx.x; i < nb; i += kBlock)
+    if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
 // One workgroup per tensor: the digit bin holding the krem-th largest key.
-__global__ __launch_bounds__(kBlock) void topk_pick(Geometry g, TopkArgs a, int shift) {
-  __shared__ uint32_t suf[257];
+// Thread b owns bins kPer b .. kPer b + kPer - 1.
+template <int kBits>
+__global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
+  constexpr int kBins = 1 << kBits, kPer = kBins / kBlock;
+  static_assert(kPer >= 1 && kBins <= kMaxBins, "digit width");
+  __shared__ uint32_t suf[kBlock + 1];
   __shared__ uint32_t krem_s;
   const int t = blockIdx.x;
   const int b = threadIdx.x;
-  uint32_t *hist = a.hist + static_cast<size_t>(t) * 256;
-  suf[b] = hist[b];
+  uint32_t *hist = a.hist + static_cast<size_t>(t) * kMaxBins;
+  uint32_t cnt[kPer];
+  uint32_t local = 0;
+  for (int j = 0; j < kPer; ++j) {
+    cnt[j] = hist[b * kPer + j];
+    local += cnt[j];
+  }
+  suf[b] = local;
   if (b == 0) {
-    suf[256] = 0u;
+    suf[kBlock] = 0u;
     krem_s = a.krem[t];   // read once, before the one writer below updates it
   }
   __syncthreads();
-  // suffix sums: suf[b] = count of keys whose digit is >= b (Hillis-Steele)
-  for (int d = 1; d < 256; d <<= 1) {
-    const uint32_t add = (b + d < 256) ? suf[b + d] : 0u;
+  // suffix sums over threads: suf[b] = keys in the bins of threads >= b (Hillis-Steele)
+  for (int d = 1; d < kBlock; d <<= 1) {
+    const uint32_t add = (b + d < kBlock) ? suf[b + d] : 0u;
     __syncthreads();
     suf[b] += add;
     __syncthreads();
   }
   const uint32_t krem = krem_s;
-  if (suf[b] >= krem && suf[b + 1] < krem) {   // exactly one bin satisfies this
-    a.prefix[t] |= static_cast<uint32_t>(b) << shift;
-    a.krem[t] = krem - suf[b + 1];
+  uint32_t above = suf[b + 1];
+  if (above < krem && suf[b] >= krem) {   // exactly one thread holds the krem-th largest
+    for (int j = kPer - 1; j >= 0; --j) {
+      if (above + cnt[j] >= krem) {
+        a.prefix[t] |= static_cast<uint32_t>(b * kPer + j) << shift;
+        a.krem[t] = krem - above;
+        break;
+      }
+      above += cnt[j];
+    }
   }
   __syncthreads();
-  hist[b] = 0u;   // ready for the next pass
+  for (int j = 0; j < kPer; ++j) hist[b * kPer + j] = 0u;   // ready for the next pass
+}
+
+// The tile's stored keys, one per lane slot (0 past the tile's end).
+template <bool kFull>
+__device__ __forceinline__ void load_keys(const TopkArgs &a, const Tile &tl, const TileLanes &ln,
+                                          uint32_t (&key)[kPerLane]) {
+  const uint32_t *keys = a.keys + ln.base + ln.lane;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    key[c] = 0u;
+    if (slot_ok<kFull>(tl, ln, c)) key[c] = keys[64 * c];
+  }
 }
 
 // ---------------------------------------------------------------------------
 // per-tile counts of keys above and at the threshold, then per-tensor offsets
 // ---------------------------------------------------------------------------
-template <typename G>
+template <bool kFull>
+__device__ __forceinline__ void count_tile(const TopkArgs &a, const Tile &tl, uint32_t tau,
+                                           uint32_t &gt, uint32_t &eq) {
+  const TileLanes ln = tile_lanes(tl);
+  uint32_t key[kPerLane];
+  load_keys<kFull>(a, tl, ln, key);
+  gt = 0;
+  eq = 0;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    const bool ok = slot_ok<kFull>(tl, ln, c);
+    gt += __popcll(__ballot(ok && key[c] > tau));
+    eq += __popcll(__ballot(ok && key[c] == tau));
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void topk_count(Geometry g, TopkArgs a) {
   __shared__ uint32_t cnt[2][kWaves];
   const Tile tl = g.tiles[blockIdx.x];
-  const TileLanes ln = tile_lanes(tl);
   const uint32_t tau = a.prefix[tl.tensor];
-  uint32_t gt = 0, eq = 0;
-  for (int c = 0; c < kPerLane; ++c) {
-    const bool ok = valid(tl, ln, c);
-    const uint32_t key = ok ? leader_key<G>(a, g, ln.base + 64 * c + ln.lane) : 0u;
-    gt += __popcll(__ballot(ok && key > tau));
-    eq += __popcll(__ballot(ok && key == tau));
-  }
-  if (ln.lane == 0) {
-    cnt[0][ln.wave] = gt;
-    cnt[1][ln.wave] = eq;
+  uint32_t gt, eq;
+  if (tl.len == kTile)
+    count_tile<true>(a, tl, tau, gt, eq);
+  else
+    count_tile<false>(a, tl, tau, gt, eq);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    cnt[0][wave] = gt;
+    cnt[1][wave] = eq;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -203,22 +285,23 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
 // ---------------------------------------------------------------------------
 // selection: bitmask, per-word positions and the ascending index list
 // ---------------------------------------------------------------------------
-template <typename G>
-__global__ __launch_bounds__(kBlock) void topk_select(Geometry g, TopkArgs a) {
-  __shared__ int64_t weq[kWaves], wsel[kWaves];
-  const Tile tl = g.tiles[blockIdx.x];
+template <bool kFull>
+__device__ __forceinline__ void select_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
+                                            int64_t *weq, int64_t *wsel) {
   const TileLanes ln = tile_lanes(tl);
   const int t = tl.tensor;
   const uint32_t tau = a.prefix[t];
   const int64_t r = a.krem[t];
-  // phase 1: keys at the threshold per wavefront
-  uint64_t gtw = 0, eqw = 0;   // lane c keeps word c of each mask
+  uint32_t key[kPerLane];
+  load_keys<kFull>(a, tl, ln, key);
+  // phase 1: keys at the threshold per wavefront; lane c keeps word c of each mask
+  uint64_t gtw = 0, eqw = 0;
   int64_t neq = 0;
+#pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
-    const bool ok = valid(tl, ln, c);
-    const uint32_t key = ok ? leader_key<G>(a, g, ln.base + 64 * c + ln.lane) : 0u;
-    const uint64_t bg = __ballot(ok && key > tau);
-    const uint64_t be = __ballot(ok && key == tau);
+    const bool ok = slot_ok<kFull>(tl, ln, c);
+    const uint64_t bg = __ballot(ok && key[c] > tau);
+    const uint64_t be = __ballot(ok && key[c] == tau);
     if (ln.lane == c) {
       gtw = bg;
       eqw = be;
@@ -232,9 +315,10 @@ __global__ __launch_bounds__(kBlock) void topk_select(Geometry g, TopkArgs a) {
   // phase 2: selected = above the threshold, or at it with tie rank < r
   uint64_t selw = 0;
   int64_t nsel = 0;
+#pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
-    const uint64_t be = __shfl(eqw, c);
-    const uint64_t bg = __shfl(gtw, c);
+    const uint64_t be = readlane64(eqw, c);
+    const uint64_t bg = readlane64(gtw, c);
     const int64_t rank = eq_run + __popcll(be & lanemask_lt(ln.lane));
     const bool take_eq = ((be >> ln.lane) & 1ull) && rank < r;
     const uint64_t bs = bg | __ballot(take_eq);
@@ -250,8 +334,9 @@ __global__ __launch_bounds__(kBlock) void topk_select(Geometry g, TopkArgs a) {
   const int64_t tensor_start =
       tl.start - static_cast<int64_t>(static_cast<int>(blockIdx.x) - g.tile_begin[t]) * kTile;
   const int64_t k_end = a.k_off[t + 1];
+#pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
-    const uint64_t bs = __shfl(selw, c);
+    const uint64_t bs = readlane64(selw, c);
     const int64_t word = (ln.base >> 6) + c;
     if (c < ln.nwords) {
       if (ln.lane == 0) {
@@ -268,10 +353,52 @@ __global__ __launch_bounds__(kBlock) void topk_select(Geometry g, TopkArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kBlock) void topk_select(Geometry g, TopkArgs a) {
+  __shared__ int64_t weq[kWaves], wsel[kWaves];
+  const Tile tl = g.tiles[blockIdx.x];
+  if (tl.len == kTile)
+    select_tile<true>(g, a, tl, weq, wsel);
+  else
+    select_tile<false>(g, a, tl, weq, wsel);
+}
+
 // ---------------------------------------------------------------------------
 // gather the messages of every worker and update the memories; workgroups are
 // (worker group, tile), group-major as in the worker passes
 // ---------------------------------------------------------------------------
+template <typename G, bool kFull>
+__device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
+                                            int w_lo, int w_hi) {
+  const TileLanes ln = tile_lanes(tl);
+  const int64_t k_end = a.k_off[tl.tensor + 1];
+  // word c of the selection mask and its first position, held by lane c
+  const uint64_t selw = ln.lane < ln.nwords ? a.sel_words[(ln.base >> 6) + ln.lane] : 0ull;
+  const int64_t posw = ln.lane < ln.nwords ? a.word_pos[(ln.base >> 6) + ln.lane] : 0;
+  for (int w = w_lo; w < w_hi; ++w) {
+    const size_t row = static_cast<size_t>(w) * g.N + ln.base + ln.lane;
+    float *mem = a.memory + row;
+    const G *gw = static_cast<const G *>(a.grads) + row;
+    float *vals = a.values + static_cast<size_t>(w) * a.K;
+    float x[kPerLane];
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c) {   // all loads first: the stores below may alias them
+      x[c] = 0.0f;
+      if (slot_ok<kFull>(tl, ln, c)) x[c] = mem[64 * c] + grad_at(gw + 64 * c);
+    }
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c) {
+      const uint64_t bs = readlane64(selw, c);
+      const bool mine = (bs >> ln.lane) & 1ull;   // never set past the tile's end
+      if (slot_ok<kFull>(tl, ln, c)) mem[64 * c] = mine ? 0.0f : x[c];
+      if (mine) {
+        const int64_t at = static_cast<int64_t>(readlane64(static_cast<uint64_t>(posw), c)) +
+                           __popcll(bs & lanemask_lt(ln.lane));
+        if (at < k_end) vals[at] = x[c];   // always true when the selection holds k_t entries
+      }
+    }
+  }
+}
+
 template <typename G>
 __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(g.num_tiles));
@@ -279,29 +406,10 @@ __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   const int w_lo = grp * a.wgroup;
   const int w_hi = min(g.W, w_lo + a.wgroup);
   const Tile tl = g.tiles[tile];
-  const TileLanes ln = tile_lanes(tl);
-  const int64_t k_end = a.k_off[tl.tensor + 1];
-  // word c of the selection mask and its first position, held by lane c
-  const uint64_t selw = ln.lane < ln.nwords ? a.sel_words[(ln.base >> 6) + ln.lane] : 0ull;
-  const int64_t posw = ln.lane < ln.nwords ? a.word_pos[(ln.base >> 6) + ln.lane] : 0;
-  for (int w = w_lo; w < w_hi; ++w) {
-    float *mem = a.memory + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
-    const G *gw = static_cast<const G *>(a.grads) + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
-    float *vals = a.values + static_cast<size_t>(w) * a.K;
-    for (int c = 0; c < kPerLane; ++c) {
-      const uint64_t bs = __shfl(selw, c);
-      const int64_t p0 = __shfl(posw, c);
-      if (!valid(tl, ln, c)) continue;
-      const float x = mem[64 * c] + grad_at(gw + 64 * c);
-      if ((bs >> ln.lane) & 1ull) {
-        const int64_t at = p0 + __popcll(bs & lanemask_lt(ln.lane));
-        if (at < k_end) vals[at] = x;   // always true when the selection holds k_t entries
-        mem[64 * c] = 0.0f;
-      } else {
-        mem[64 * c] = x;
-      }
-    }
-  }
+  if (tl.len == kTile)
+    gather_tile<G, true>(g, a, tl, w_lo, w_hi);
+  else
+    gather_tile<G, false>(g, a, tl, w_lo, w_hi);
 }
 
 // the server: average of the W messages, ascending workers from +0, then / W
@@ -316,35 +424,51 @@ __global__ __launch_bounds__(kBlock) void topk_average(TopkArgs a, int W) {
 }
 
 template <typename G>
-void launch_topk_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
-  const dim3 block(kBlock), tiles(g.num_tiles);
-  const int64_t resets = static_cast<int64_t>(g.T) * 256;
+void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
+  const dim3 block(kBlock), tiles(g.num_tiles), tensors(g.T);
+  const int64_t resets = static_cast<int64_t>(g.T) * kMaxBins;
   hipLaunchKernelGGL(topk_reset, dim3(static_cast<unsigned>((resets + kBlock - 1) / kBlock)), block,
                      0, s, g, a);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hipLaunchKernelGGL(topk_hist<G>, tiles, block, 0, s, g, a, shift);
-    hipLaunchKernelGGL(topk_pick, dim3(g.T), block, 0, s, g, a, shift);
-  }
-  hipLaunchKernelGGL(topk_count<G>, tiles, block, 0, s, g, a);
-  hipLaunchKernelGGL(topk_offsets, dim3(g.T), block, 0, s, g, a);
-  hipLaunchKernelGGL(topk_select<G>, tiles, block, 0, s, g, a);
-  const int groups = (g.W + a.wgroup - 1) / a.wgroup;
-  hipLaunchKernelGGL(topk_gather<G>, dim3(static_cast<unsigned>(g.num_tiles) * groups), block, 0, s,
-                     g, a);
-  const dim3 avg_grid(static_cast<unsigned>((a.K + kBlock - 1) / kBlock));
-  if ((g.W & (g.W - 1)) == 0)
-    hipLaunchKernelGGL(topk_average<true>, avg_grid, block, 0, s, a, g.W);
-  else
-    hipLaunchKernelGGL(topk_average<false>, avg_grid, block, 0, s, a, g.W);
+  hipLaunchKernelGGL((topk_hist<G, true>), tiles, block, 0, s, g, a, kShift0, 11);
+  hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift0);
+  hipLaunchKernelGGL((topk_hist<G, false>), tiles, block, 0, s, g, a, kShift1, 11);
+  hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift1);
+  hipLaunchKernelGGL((topk_hist<G, false>), tiles, block, 0, s, g, a, kShift2, 9);
+  hipLaunchKernelGGL(topk_pick<9>, tensors, block, 0, s, a, kShift2);
+  hipLaunchKernelGGL(topk_count, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);
+  hipLaunchKernelGGL(topk_select, tiles, block, 0, s, g, a);
 }
 
 }  // namespace
 
-void launch_topk(const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s) {
-  if (bf16)
-    launch_topk_typed<uint16_t>(g, a, s);
-  else
-    launch_topk_typed<float>(g, a, s);
+void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s) {
+  const dim3 block(kBlock);
+  switch (stage) {
+    case TopkStage::kSelect:
+      if (bf16)
+        launch_select_typed<uint16_t>(g, a, s);
+      else
+        launch_select_typed<float>(g, a, s);
+      break;
+    case TopkStage::kGather: {
+      const int groups = (g.W + a.wgroup - 1) / a.wgroup;
+      const dim3 grid(static_cast<unsigned>(g.num_tiles) * groups);
+      if (bf16)
+        hipLaunchKernelGGL(topk_gather<uint16_t>, grid, block, 0, s, g, a);
+      else
+        hipLaunchKernelGGL(topk_gather<float>, grid, block, 0, s, g, a);
+      break;
+    }
+    case TopkStage::kAverage: {
+      const dim3 grid(static_cast<unsigned>((a.K + kBlock - 1) / kBlock));
+      if ((g.W & (g.W - 1)) == 0)
+        hipLaunchKernelGGL(topk_average<true>, grid, block, 0, s, a, g.W);
+      else
+        hipLaunchKernelGGL(topk_average<false>, grid, block, 0, s, a, g.W);
+      break;
+    }
+  }
 }
 
 }  // namespace ob
