@@ -26,7 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "compressed optimizer-step elements/s and HBM GB/s (% of peak), 1 MI355X"
-KERNELS_SRC = os.path.join(ROOT, "error_compensated_bit_02_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "error_compensated_bit_02_amd", "csrc")
+SOURCES = ("kernels.hip", "topk.hip")   # the device code whose traffic the counters measured
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
 
 
@@ -54,7 +55,7 @@ def kernel_bytes_per_element(wl) -> dict:
         "worker_pass1": 4.0 + (g + 4.0) * W + W / 8.0,        # read m, g, e; write signs
         "worker_pass2": 4.0 + (g + 4.0) * W + 4.0 * W,        # read m, g, e; write e
         "server_pass1": W / 8.0 + 4.0,                        # read signs, e_s
-        "server_pass2_update": W / 8.0 + 16.0 + 12.0 + 1 / 8.0,  # read signs, e_s, v, p; write e_s, m, p, signs
+        "server_pass2_update": W / 8.0 + 12.0 + 12.0 + 1 / 8.0,  # read signs, e_s, v, p; write e_s, m, p, signs
         "server_pass2": W / 8.0 + 8.0 + 1 / 8.0,              # read signs, e_s; write e_s, signs
         "apply_update": 1 / 8.0 + 16.0,                       # read signs, v, p; write m, p
         "trust_norms": 1 / 8.0 + 8.0,                         # read signs, v, p
@@ -70,27 +71,104 @@ def cltk_bytes_per_element(wl, density: float) -> dict:
     move, its own operands touched once (density d = kept fraction)."""
     W, g, d = wl.workers, grad_bytes(wl), density
     return {
-        "cltk_select": g + 4.0 + 4.0 * d,          # read the leader's memory and gradient; write index
-        "cltk_gather": (g + 8.0) * W + 4.0 * d * W,  # read memory and gradient, write memory; write values
+        "cltk_select": g + 4.0,                    # read the leader's memory and gradient
+        # read memory and gradient, write memory; write values and the index list
+        "cltk_gather": (g + 8.0) * W + 4.0 * d * W + 4.0 * d,
         "cltk_average": d * (4.0 * W + 4.0),       # read values, write the average
     }
+
+
+def source_of(kernel: str) -> str:
+    return "topk.hip" if kernel.startswith("cltk_") else "kernels.hip"
+
+
+def sha256_of(name: str) -> str:
+    import hashlib
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def counter_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
-    reading), or None when there is none or the kernels changed since."""
-    import hashlib
+    reading), or None when there is none or the kernel's source changed since."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    with open(KERNELS_SRC, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != data.get("kernels_hip_sha256"):
-            return None
+    src = source_of(kernel)
+    if data.get("sources_sha256", {}).get(src) != sha256_of(src):
+        return None
     per = data.get("per_launch_bytes", {}).get(kernel)
     return None if per is None else float(per)
+
+
+# rocprofv3 kernel names -> the library's kernel kinds.  The CLT-k select
+# stage is ten launches; its bytes are summed per exchange (per topk_reset).
+_SELECT_STAGE = ("topk_reset", "topk_hist", "topk_pick", "topk_count", "topk_offsets", "topk_select")
+
+
+def kind_of(name: str):
+    import re
+    m = re.search(r"ob::\(anonymous namespace\)::(\w+)(?:<([^>]*)>)?", name)
+    if not m:
+        return "copy" if "copyBuffer" in name else None
+    base, args = m.group(1), [x.strip() for x in (m.group(2) or "").split(",")]
+    if base == "worker_kernel":
+        return ("worker_pass1", "worker_pass2", "worker_residual_first", "worker_residual")[int(args[1])]
+    if base == "server_kernel":
+        return ("server_pass1", "server_pass2", "server_pass2_update", "server_residual_first",
+                "server_residual")[int(args[0])]
+    if base == "update_kernel":
+        return "apply_update" if args[0] == "true" else "update_residual"
+    if base in _SELECT_STAGE:
+        return "cltk_select"
+    if base == "topk_gather":
+        return "cltk_gather"
+    if base == "topk_average":
+        return "cltk_average"
+    return base
+
+
+def summarize_counters(pmc_dir: str, workload: str) -> dict:
+    """Turn rocprofv3 --pmc CSVs into per-launch HBM bytes.  Expects
+    {pmc_dir}/step_FETCH_SIZE, step_WRITE_SIZE (bench.py runs) and
+    copy_FETCH_SIZE, copy_WRITE_SIZE (bench.py --copy-calibration 1024)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def load(tag):
+        files = glob.glob(os.path.join(pmc_dir, tag, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(pmc_dir, tag)}")
+        total, resets = defaultdict(float), 0
+        launches = defaultdict(int)
+        for path in files:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = kind_of(r["Kernel_Name"])
+                    if k is None:
+                        continue
+                    total[k] += float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
+                    launches[k] += 1
+                    resets += "topk_reset" in r["Kernel_Name"]
+        if resets:
+            launches["cltk_select"] = resets   # one select stage per exchange
+        return {k: total[k] / launches[k] for k in total}
+
+    copy_bytes = 1024 << 20
+    fetch_factor = copy_bytes / load("copy_FETCH_SIZE")["copy"]
+    write_factor = copy_bytes / load("copy_WRITE_SIZE")["copy"]
+    fetch, write = load("step_FETCH_SIZE"), load("step_WRITE_SIZE")
+    per = {k: round(fetch[k] * fetch_factor + write.get(k, 0.0) * write_factor)
+           for k in fetch if k != "copy"}
+    return {"workload": workload, "sources_sha256": {s: sha256_of(s) for s in SOURCES},
+            "fetch_factor": fetch_factor, "write_factor": write_factor,
+            "copy_calibration_bytes": copy_bytes, "per_launch_bytes": per,
+            "per_launch_fetch_bytes": {k: round(fetch[k] * fetch_factor) for k in per},
+            "per_launch_write_bytes": {k: round(write.get(k, 0.0) * write_factor) for k in per}}
 
 
 def cpu_baseline(wl, state, grads, sample_tensors: int) -> dict:
@@ -257,11 +335,23 @@ def main() -> int:
                          "each tensor (0 = skip)")
     ap.add_argument("--cpu-sample-tensors", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
+                    help="write profiles/<workload>_hbm_counters.json from rocprofv3 --pmc runs "
+                         "under PMC_DIR (no GPU needed), then exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 launches) for calibrating "
                          "HBM byte counters, then exit")
     args = ap.parse_args()
 
+    if args.summarize_counters:
+        data = summarize_counters(args.summarize_counters, args.workload)
+        out = os.path.join(ROOT, "profiles", f"{args.workload}_hbm_counters.json")
+        with open(out, "w") as f:
+            json.dump(data, f, indent=1)
+        log(f"bench: wrote {out}")
+        for k, v in sorted(data["per_launch_bytes"].items()):
+            log(f"  {k:24s} {v / 1e9:9.3f} GB per launch")
+        return 0
     if args.gpus != 1:
         log(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "
             f"(all W simulated workers share one GPU's HBM)")

@@ -519,9 +519,9 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t T = static_cast<size_t>(c->T), tiles = static_cast<size_t>(c->num_tiles);
   const size_t nw = static_cast<size_t>(c->N / 64);
-  const size_t sizes[] = {up((T + 1) * 8), up(T * 2048 * 4), up(T * 4),  up(T * 4),
+  const size_t sizes[] = {up((T + 1) * 8), up(T * 2048 * 4), up(T * 4),     up(T * 4),
                           up(tiles * 4),     up(tiles * 4),    up(tiles * 8), up(tiles * 8),
-                          up(nw * 8),        up(nw * 8),       up(nw * 64 * 4)};
+                          up(nw * 64 * 4)};
   size_t total = 0;
   for (size_t b : sizes) total += b;
   if (c->topk_scratch) {
@@ -549,9 +549,7 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   a.tile_eq = reinterpret_cast<uint32_t *>(at[5]);
   a.tile_eq_before = reinterpret_cast<int64_t *>(at[6]);
   a.tile_sel_off = reinterpret_cast<int64_t *>(at[7]);
-  a.sel_words = reinterpret_cast<uint64_t *>(at[8]);
-  a.word_pos = reinterpret_cast<int64_t *>(at[9]);
-  a.keys = reinterpret_cast<uint32_t *>(at[10]);
+  a.keys = reinterpret_cast<uint32_t *>(at[8]);
   a.K = k_off[T];
   if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess)
     return OB_ERR_DEVICE;

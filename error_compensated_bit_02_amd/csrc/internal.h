@@ -168,15 +168,13 @@ struct TopkArgs {
   uint32_t *tile_eq;         // [num_tiles] keys at the threshold
   int64_t *tile_eq_before;   // [num_tiles] keys at the threshold in earlier tiles of the tensor
   int64_t *tile_sel_off;     // [num_tiles] position of the tile's first selected entry
-  uint64_t *sel_words;       // [Nw] selection bitmask (bit l of word j: element 64 j + l)
-  int64_t *word_pos;         // [Nw] position of each word's first selected entry
   int leader;                // worker whose values rank the positions
   int wgroup;                // workers per workgroup in the gather pass
 };
 
-// The codec's three stages: the leader's selection (radix select, offsets,
-// index list), the gather of every worker's message with the memory update,
-// and the server's average.
+// The codec's three stages: the leader's threshold (radix select, per-tile
+// counts and offsets), the selection with the index list and the gather of
+// every worker's message with the memory update, and the server's average.
 enum class TopkStage { kSelect, kGather, kAverage };
 void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s);
 

@@ -10,9 +10,10 @@
 // and 9-bit digits (per-tile LDS histograms added into per-tensor
 // histograms); the first pass also stores the keys, so the later passes read
 // 4 bytes per element instead of the leader's memory and gradient.  Ties at
-// that key go to the lowest indices, and the positions are written in
-// ascending order through per-tile offsets.  Then one dense pass over all
-// workers gathers the messages and updates the memories, and the server
+// that key go to the lowest indices; per-tile counts and per-tensor scans
+// give each tile its first position.  Then one dense pass over all workers
+// rebuilds each tile's selection from the keys, writes the ascending index
+// list, gathers the messages and updates the memories, and the server
 // averages the W messages in ascending worker order.
 //
 // The element mapping is the one of kernels.hip: a workgroup of 4
@@ -283,18 +284,23 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// selection: bitmask, per-word positions and the ascending index list
+// selection and gather.  Workgroups are (worker group, tile), group-major as
+// in the worker passes.  Each rebuilds its tile's selection from the stored
+// keys (read-only here, so groups need no ordering): selected = key above the
+// threshold, or at it with tie rank < r; lane c of each wavefront keeps word
+// c of the mask and the position of its first selected entry.  The first
+// group writes the index list; every group then streams its workers.
 // ---------------------------------------------------------------------------
 template <bool kFull>
-__device__ __forceinline__ void select_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                            int64_t *weq, int64_t *wsel) {
-  const TileLanes ln = tile_lanes(tl);
+__device__ __forceinline__ void select_words(const Geometry &g, const TopkArgs &a, const Tile &tl,
+                                             int tile, const TileLanes &ln, int64_t *wcnt,
+                                             bool write_index, uint64_t &selw, int64_t &posw) {
   const int t = tl.tensor;
   const uint32_t tau = a.prefix[t];
   const int64_t r = a.krem[t];
   uint32_t key[kPerLane];
   load_keys<kFull>(a, tl, ln, key);
-  // phase 1: keys at the threshold per wavefront; lane c keeps word c of each mask
+  // keys at the threshold per wavefront; lane c keeps word c of each mask
   uint64_t gtw = 0, eqw = 0;
   int64_t neq = 0;
 #pragma unroll
@@ -308,12 +314,12 @@ __device__ __forceinline__ void select_tile(const Geometry &g, const TopkArgs &a
     }
     neq += __popcll(be);
   }
-  if (ln.lane == 0) weq[ln.wave] = neq;
+  if (ln.lane == 0) wcnt[ln.wave] = neq;
   __syncthreads();
-  int64_t eq_run = a.tile_eq_before[blockIdx.x];
-  for (int v = 0; v < ln.wave; ++v) eq_run += weq[v];
-  // phase 2: selected = above the threshold, or at it with tie rank < r
-  uint64_t selw = 0;
+  int64_t eq_run = a.tile_eq_before[tile];
+  for (int v = 0; v < ln.wave; ++v) eq_run += wcnt[v];
+  __syncthreads();   // wcnt is reused below
+  selw = 0;
   int64_t nsel = 0;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
@@ -326,54 +332,36 @@ __device__ __forceinline__ void select_tile(const Geometry &g, const TopkArgs &a
     eq_run += __popcll(be);
     nsel += __popcll(bs);
   }
-  if (ln.lane == 0) wsel[ln.wave] = nsel;
+  if (ln.lane == 0) wcnt[ln.wave] = nsel;
   __syncthreads();
-  int64_t pos = a.tile_sel_off[blockIdx.x];
-  for (int v = 0; v < ln.wave; ++v) pos += wsel[v];
-  // phase 3: positions in ascending index order (index = position within the tensor)
+  int64_t pos = a.tile_sel_off[tile];
+  for (int v = 0; v < ln.wave; ++v) pos += wcnt[v];
+  // positions in ascending index order (index = position within the tensor)
   const int64_t tensor_start =
-      tl.start - static_cast<int64_t>(static_cast<int>(blockIdx.x) - g.tile_begin[t]) * kTile;
+      tl.start - static_cast<int64_t>(tile - g.tile_begin[t]) * kTile;
   const int64_t k_end = a.k_off[t + 1];
+  posw = 0;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     const uint64_t bs = readlane64(selw, c);
-    const int64_t word = (ln.base >> 6) + c;
-    if (c < ln.nwords) {
-      if (ln.lane == 0) {
-        a.sel_words[word] = bs;
-        a.word_pos[word] = pos;
-      }
-      if ((bs >> ln.lane) & 1ull) {
-        const int64_t at = pos + __popcll(bs & lanemask_lt(ln.lane));
-        if (at < k_end)   // always true when the selection holds k_t entries
-          a.index[at] = static_cast<int32_t>(ln.base + 64 * c + ln.lane - tensor_start);
-      }
+    if (ln.lane == c) posw = pos;
+    if (write_index && ((bs >> ln.lane) & 1ull)) {
+      const int64_t at = pos + __popcll(bs & lanemask_lt(ln.lane));
+      if (at < k_end)   // always true when the selection holds k_t entries
+        a.index[at] = static_cast<int32_t>(ln.base + 64 * c + ln.lane - tensor_start);
     }
     pos += __popcll(bs);
   }
 }
 
-__global__ __launch_bounds__(kBlock) void topk_select(Geometry g, TopkArgs a) {
-  __shared__ int64_t weq[kWaves], wsel[kWaves];
-  const Tile tl = g.tiles[blockIdx.x];
-  if (tl.len == kTile)
-    select_tile<true>(g, a, tl, weq, wsel);
-  else
-    select_tile<false>(g, a, tl, weq, wsel);
-}
-
-// ---------------------------------------------------------------------------
-// gather the messages of every worker and update the memories; workgroups are
-// (worker group, tile), group-major as in the worker passes
-// ---------------------------------------------------------------------------
 template <typename G, bool kFull>
 __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                            int w_lo, int w_hi) {
+                                            int tile, int w_lo, int w_hi, int64_t *wcnt) {
   const TileLanes ln = tile_lanes(tl);
   const int64_t k_end = a.k_off[tl.tensor + 1];
-  // word c of the selection mask and its first position, held by lane c
-  const uint64_t selw = ln.lane < ln.nwords ? a.sel_words[(ln.base >> 6) + ln.lane] : 0ull;
-  const int64_t posw = ln.lane < ln.nwords ? a.word_pos[(ln.base >> 6) + ln.lane] : 0;
+  uint64_t selw;
+  int64_t posw;
+  select_words<kFull>(g, a, tl, tile, ln, wcnt, w_lo == 0, selw, posw);
   for (int w = w_lo; w < w_hi; ++w) {
     const size_t row = static_cast<size_t>(w) * g.N + ln.base + ln.lane;
     float *mem = a.memory + row;
@@ -401,15 +389,16 @@ __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a
 
 template <typename G>
 __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
+  __shared__ int64_t wcnt[kWaves];
   const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(g.num_tiles));
   const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(g.num_tiles));
   const int w_lo = grp * a.wgroup;
   const int w_hi = min(g.W, w_lo + a.wgroup);
   const Tile tl = g.tiles[tile];
   if (tl.len == kTile)
-    gather_tile<G, true>(g, a, tl, w_lo, w_hi);
+    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt);
   else
-    gather_tile<G, false>(g, a, tl, w_lo, w_hi);
+    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt);
 }
 
 // the server: average of the W messages, ascending workers from +0, then / W
@@ -437,7 +426,6 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(topk_pick<9>, tensors, block, 0, s, a, kShift2);
   hipLaunchKernelGGL(topk_count, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);
-  hipLaunchKernelGGL(topk_select, tiles, block, 0, s, g, a);
 }
 
 }  // namespace
