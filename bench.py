@@ -290,6 +290,42 @@ def summarize_cltk(wl, n_elem, steps, dt, kernels, density, workload):
     }
 
 
+def copy_ceiling(gib: int = 4, reps: int = 5) -> dict:
+    """A plain device-to-device copy of `gib` GiB, timed with events on torch's
+    stream: the streaming rate a read+write kernel can reach on this machine."""
+    import torch
+    n = gib << 28                      # fp32 elements
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    best = sorted(ms)[len(ms) // 2]
+    return {"gbps": round(2 * 4 * n / (best * 1e-3) / 1e9, 1), "bytes_copied": 4 * n,
+            "median_ms": round(best, 4), "reps": reps, "frac": round(2 * 4 * n / (best * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def step_counter_gbps(workload, per_kernel, ms_step, steps):
+    """Whole-step HBM GB/s from the counter bytes of every kernel the step
+    launched, or None when some kernel has no current counter figure."""
+    total = 0.0
+    for k, v in per_kernel.items():
+        if not v["launches"]:
+            continue
+        b = counter_traffic(workload, k)
+        if b is None:
+            return None
+        total += b * v["launches"] / steps
+    return round(total / (ms_step * 1e-3) / 1e9, 1)
+
+
 def summarize(wl, n_elem, steps, dt, kernels, workload):
     ms_step = dt * 1e3 / steps
     b_alg = step_bytes_per_element(wl)
@@ -305,10 +341,13 @@ def summarize(wl, n_elem, steps, dt, kernels, workload):
                 "traffic": None if traffic is None else round(traffic),
                 "algorithmic_bytes": round(kb[dom] * n_elem),
                 "bytes_per_element": kb[dom], "avg_ms": round(dom_ms, 4)}
+    counter_gbps = step_counter_gbps(workload, per_kernel, ms_step, steps)
     return {
         "ms_per_step": ms_step,
         "value": n_elem * steps / dt,
         "step_hbm_gbps_algorithmic": round(step_gbps, 1),
+        "step_hbm_gbps_counter": counter_gbps,
+        "step_counter_frac_of_peak": None if counter_gbps is None else round(counter_gbps / HBM_PEAK_GBPS, 4),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
@@ -418,6 +457,8 @@ def main() -> int:
                    "trust_ratio_weight_decay": args.trust_ratio},
         "step_hbm_gbps_algorithmic": head["step_hbm_gbps_algorithmic"],
         "step_frac_of_peak": head["step_frac_of_peak"],
+        "step_hbm_gbps_counter": head["step_hbm_gbps_counter"],
+        "step_counter_frac_of_peak": head["step_counter_frac_of_peak"],
         "step_bytes_per_element": step_bytes_per_element(wl),
         "worker_elements_per_s": head["value"] * wl.workers,
         "roofline": head["roofline"],
@@ -426,6 +467,8 @@ def main() -> int:
     if "strict" in results and forms[0] != "strict":
         result["strict_form"] = results["strict"]
     result["cltk"] = cltk
+    torch.cuda.empty_cache()
+    result["copy_ceiling"] = copy_ceiling()
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (cpu baseline)")
