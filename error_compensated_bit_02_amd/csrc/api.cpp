@@ -273,17 +273,29 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->off = off;
   c->N = off[num_tensors];
 
+  // The largest launches must fit the device's grid limit: (worker group,
+  // tile) workgroups, and the scale finalize's one wavefront per (worker, tensor).
+  int64_t nt = 0;
+  for (int32_t t = 0; t < num_tensors; ++t) nt += (numel[t] + ob::kTile - 1) / ob::kTile;
+  if (nt > ob::kMaxGrid) {
+    delete c;
+    return OB_ERR_INVALID;
+  }
+  const int64_t wgroup = ob::worker_group_size(num_workers, static_cast<int>(nt));
+  const int64_t finalize = (static_cast<int64_t>(num_workers) * num_tensors + ob::kWaves - 1) / ob::kWaves;
+  if (nt * ((num_workers + wgroup - 1) / wgroup) > ob::kMaxGrid || finalize > ob::kMaxGrid) {
+    delete c;
+    return OB_ERR_INVALID;
+  }
+
   std::vector<ob::Tile> tiles;
+  tiles.reserve(static_cast<size_t>(nt));
   std::vector<int32_t> tile_begin(static_cast<size_t>(num_tensors) + 1);
   for (int32_t t = 0; t < num_tensors; ++t) {
     tile_begin[t] = static_cast<int32_t>(tiles.size());
     for (int64_t k = 0; k < numel[t]; k += ob::kTile) {
       const int64_t len = numel[t] - k < ob::kTile ? numel[t] - k : ob::kTile;
       tiles.push_back(ob::Tile{off[t] + k, static_cast<int32_t>(len), t});
-    }
-    if (tiles.size() > 0x7fffffffu) {
-      delete c;
-      return OB_ERR_INVALID;
     }
   }
   tile_begin[num_tensors] = static_cast<int32_t>(tiles.size());

@@ -102,6 +102,10 @@ struct WorkerArgs {
 // launches of a small list would leave most of the 256 CUs idle at the tail).
 constexpr int kMaxGroup = OB_MAX_GROUP;
 constexpr int kMinBlocks = 8192;
+// A launch's work-items per dimension must fit in 32 bits: at most this many
+// workgroups of kBlock threads.
+constexpr int64_t kMaxGrid = 0xffffffffLL / kBlock;
+
 inline int worker_group_size(int workers, int num_tiles) {
   int groups = (workers + kMaxGroup - 1) / kMaxGroup;
   const int want = (kMinBlocks + num_tiles - 1) / num_tiles;

@@ -84,12 +84,19 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
 constexpr int kMaxBins = 2048;
 constexpr int kShift0 = 20, kShift1 = 9, kShift2 = 0;
 
+// Grid-stride launches (grid capped at kStrideBlocks) for the two kernels
+// whose size is not a tile count.
+constexpr unsigned kStrideBlocks = 65535;
+
 __global__ __launch_bounds__(kBlock) void topk_reset(Geometry g, TopkArgs a) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (i < static_cast<int64_t>(g.T) * kMaxBins) a.hist[i] = 0u;
-  if (i < g.T) {
-    a.prefix[i] = 0u;
-    a.krem[i] = static_cast<uint32_t>(a.k_off[i + 1] - a.k_off[i]);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+       i < static_cast<int64_t>(g.T) * kMaxBins; i += stride) {
+    a.hist[i] = 0u;
+    if (i < g.T) {
+      a.prefix[i] = 0u;
+      a.krem[i] = static_cast<uint32_t>(a.k_off[i + 1] - a.k_off[i]);
+    }
   }
 }
 
@@ -404,20 +411,25 @@ __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
 // the server: average of the W messages, ascending workers from +0, then / W
 template <bool kPow2>
 __global__ __launch_bounds__(kBlock) void topk_average(TopkArgs a, int W) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  if (j >= a.K) return;
-  float acc = 0.0f;
-  for (int w = 0; w < W; ++w) acc = acc + a.values[static_cast<size_t>(w) * a.K + j];
   const float wf = static_cast<float>(W);
-  a.average[j] = kPow2 ? acc * (1.0f / wf) : acc / wf;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < a.K; j += stride) {
+    float acc = 0.0f;
+    for (int w = 0; w < W; ++w) acc = acc + a.values[static_cast<size_t>(w) * a.K + j];
+    a.average[j] = kPow2 ? acc * (1.0f / wf) : acc / wf;
+  }
+}
+
+unsigned stride_grid(int64_t items) {
+  const int64_t blocks = (items + kBlock - 1) / kBlock;
+  return static_cast<unsigned>(blocks < kStrideBlocks ? blocks : kStrideBlocks);
 }
 
 template <typename G>
 void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   const dim3 block(kBlock), tiles(g.num_tiles), tensors(g.T);
-  const int64_t resets = static_cast<int64_t>(g.T) * kMaxBins;
-  hipLaunchKernelGGL(topk_reset, dim3(static_cast<unsigned>((resets + kBlock - 1) / kBlock)), block,
-                     0, s, g, a);
+  hipLaunchKernelGGL(topk_reset, dim3(stride_grid(static_cast<int64_t>(g.T) * kMaxBins)), block, 0,
+                     s, g, a);
   hipLaunchKernelGGL((topk_hist<G, true>), tiles, block, 0, s, g, a, kShift0, 11);
   hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift0);
   hipLaunchKernelGGL((topk_hist<G, false>), tiles, block, 0, s, g, a, kShift1, 11);
@@ -449,7 +461,7 @@ void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &
       break;
     }
     case TopkStage::kAverage: {
-      const dim3 grid(static_cast<unsigned>((a.K + kBlock - 1) / kBlock));
+      const dim3 grid(stride_grid(a.K));
       if ((g.W & (g.W - 1)) == 0)
         hipLaunchKernelGGL(topk_average<true>, grid, block, 0, s, a, g.W);
       else

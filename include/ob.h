@@ -83,14 +83,20 @@ const char *ob_status_string(int status);
 
 /* Host only (no device access).  Fills elem_off[0..T] with the padded layout
  * described above for numel[0..T-1].  Returns OB_ERR_INVALID if T < 1, a
- * pointer is NULL or some numel[t] < 1. */
+ * pointer is NULL or some numel[t] is < 1 or > 2^40. */
 int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off);
 
 /* Creates a context for T tensors of numel[] elements (host array, copied),
- * W >= 1 simulated workers, gradients of grad_dtype, and the fixed
+ * 1 <= W <= 4096 simulated workers, gradients of grad_dtype, and the fixed
  * hyper-parameters beta1 (momentum, in [0, 1)) and eps (> 0).  Allocates the
- * context's device scratch on the current HIP device and uploads its tile
- * table with one synchronous copy: the only blocking call of this library. */
+ * context's device scratch on the current HIP device and uploads its tables
+ * with synchronous copies.  OB_ERR_INVALID also when a launch over the list
+ * would exceed the device's grid limit (2^32 - 1 work-items, i.e. 16,777,215
+ * workgroups of 256): the (worker group, tile) grid of 8192-element tiles,
+ * or one wavefront per (worker, tensor) for the scales.  OB_ERR_NOMEM when the
+ * scratch cannot be allocated.  Blocking calls of this library: ob_init,
+ * ob_destroy, ob_set_server_chunks, ob_cltk_configure and ob_profile_read;
+ * every other call only enqueues work on the given stream. */
 int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num_workers,
             int32_t grad_dtype, double beta1, double eps);
 

@@ -79,6 +79,19 @@ def test_init_argument_checks_fail_before_device_work(lib):
     assert lib.ob_init(ctypes.byref(ctx), 2, n, 4, 0, 0.9, 0.0) == 1        # eps = 0
     assert lib.ob_init(ctypes.byref(ctx), 2, (ctypes.c_int64 * 2)(100, 0), 4, 0, 0.9, 1e-8) == 1
     assert lib.ob_init(None, 2, n, 4, 0, 0.9, 1e-8) == 1
+    assert lib.ob_init(ctypes.byref(ctx), 2, n, 4097, 0, 0.9, 1e-8) == 1    # W > 4096
+    assert ctx.value is None
+
+
+def test_init_rejects_lists_beyond_the_grid_limit(lib):
+    """Checked on the host before any device call: 2^40 elements is 2^27 tiles
+    of 8192, beyond 16,777,215 workgroups; 4096 workers x 20,000 tensors needs
+    81.92 M scale wavefronts, 20.48 M workgroups of 4."""
+    ctx = ctypes.c_void_p()
+    big = (ctypes.c_int64 * 1)(1 << 40)
+    assert lib.ob_init(ctypes.byref(ctx), 1, big, 1, 0, 0.9, 1e-8) == 1
+    many = (ctypes.c_int64 * 20000)(*([1] * 20000))
+    assert lib.ob_init(ctypes.byref(ctx), 20000, many, 4096, 0, 0.9, 1e-8) == 1
     assert ctx.value is None
     # calls on a NULL context are rejected, nothing is launched
     assert lib.ob_step(None, *([None] * 10), 1e-4, None) == 1
