@@ -112,7 +112,10 @@ class OneBitAdam:
     Buffers (all contiguous device tensors in the padded layout):
       grads [W][N] float32 or bfloat16; m, v, params, err_s [N] float32;
       err_w [W][N] float32; packed_w [W][Nw] int64 (sign words);
-      scale_w [W][T] float32; packed_s [Nw] int64; scale_s [T] float32.
+      scale_w [W][T] float32; packed_s [Nw] int64; scale_s [S] float32
+      (S = T, or one per tensor chunk after set_server_chunks).
+      CLT-k codec (after cltk_configure): memory [W][N] float32; index [K]
+      int32; values [W][K] float32; average [K] float32.
     """
 
     def __init__(self, numel: Sequence[int], workers: int, grad_dtype: str = "f32",

@@ -11,7 +11,9 @@
  * 1 and 3).  The review's system exchanges the compressed messages with
  * custom collectives (Proposed method, bullet 4).  Here all W workers'
  * buffers live in one GPU's HBM and the exchange is a local reduction over
- * the W packed messages.
+ * the W packed messages.  Declared below with their sources as well: the
+ * warmup phase and the switch to compression, a partitioned server, a
+ * layer-wise trust ratio, and ScaleCom's cyclic local top-k codec.
  *
  * Arithmetic (the pages give no formulas; these are the readings taken):
  *   c1 = fp32(beta1), c2 = fp32(1 - beta1) (complement in double, rounded once)
@@ -41,7 +43,9 @@
  *
  * Ownership.  The caller owns every buffer passed in: device memory (HBM)
  * pointers, each aligned to 16 bytes.  The library owns only the context and
- * its scratch (a tile table and per-tile partial sums, allocated in ob_init).
+ * its scratch: a tile table, server-piece tables and per-tile partial sums
+ * (allocated in ob_init), and the CLT-k codec's keys, histograms and per-tile
+ * counts (allocated in ob_cltk_configure); ob_destroy frees both.
  *
  * Streams.  Every device call enqueues its kernels on the given stream (a
  * hipStream_t; NULL means the null stream) and returns without waiting.
