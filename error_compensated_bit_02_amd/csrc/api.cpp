@@ -533,7 +533,7 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   const size_t nw = static_cast<size_t>(c->N / 64);
   const size_t sizes[] = {up((T + 1) * 8), up(T * 2048 * 4), up(T * 4),     up(T * 4),
                           up(tiles * 4),     up(tiles * 4),    up(tiles * 8), up(tiles * 8),
-                          up(nw * 64 * 4)};
+                          up(nw * 64 * 4),   up(nw * 64 * 4),  up(tiles * 4)};
   size_t total = 0;
   for (size_t b : sizes) total += b;
   if (c->topk_scratch) {
@@ -562,6 +562,8 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   a.tile_eq_before = reinterpret_cast<int64_t *>(at[6]);
   a.tile_sel_off = reinterpret_cast<int64_t *>(at[7]);
   a.keys = reinterpret_cast<uint32_t *>(at[8]);
+  a.cand = reinterpret_cast<uint32_t *>(at[9]);
+  a.tile_m = reinterpret_cast<uint32_t *>(at[10]);
   a.K = k_off[T];
   if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess)
     return OB_ERR_DEVICE;

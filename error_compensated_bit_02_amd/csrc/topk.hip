@@ -8,10 +8,13 @@
 // selection is exact: the k-th largest key (the bit pattern of |x|, which
 // orders non-negative floats) is found by a 3-pass radix select with 11, 11
 // and 9-bit digits (per-tile LDS histograms added into per-tensor
-// histograms); the first pass also stores the keys, so the later passes read
-// 4 bytes per element instead of the leader's memory and gradient.  Ties at
-// that key go to the lowest indices; per-tile counts and per-tensor scans
-// give each tile its first position.  Then one dense pass over all workers
+// histograms).  The first pass stores the keys; the second reads them,
+// counts per tile the keys above the first digit's bin and compacts the
+// tile's keys inside that bin into a candidate list; the third pass and the
+// per-tile counts at the threshold read only the candidates (a small fraction
+// of the keys unless many keys share the top 11 bits).  Ties at the threshold
+// go to the lowest indices; per-tensor scans give each tile its first
+// position.  Then one dense pass over all workers
 // rebuilds each tile's selection from the keys, writes the ascending index
 // list, gathers the messages and updates the memories, and the server
 // averages the W messages in ascending worker order.
@@ -100,49 +103,140 @@ __global__ __launch_bounds__(kBlock) void topk_reset(Geometry g, TopkArgs a) {
   }
 }
 
-template <typename G, bool kFirst, bool kFull>
-__device__ __forceinline__ void hist_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                          uint32_t *h, int shift, int nb, uint32_t hi_mask,
-                                          uint32_t want) {
+// The tile's stored keys, one per lane slot (0 past the tile's end).
+template <bool kFull>
+__device__ __forceinline__ void load_keys(const TopkArgs &a, const Tile &tl, const TileLanes &ln,
+                                          uint32_t (&key)[kPerLane]) {
+  const uint32_t *keys = a.keys + ln.base + ln.lane;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    key[c] = 0u;
+    if (slot_ok<kFull>(tl, ln, c)) key[c] = keys[64 * c];
+  }
+}
+
+// Pass 1: the keys from the leader's memory and gradient, stored, and the
+// histogram of their top 11 bits.
+template <typename G, bool kFull>
+__device__ __forceinline__ void hist0_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
+                                           uint32_t *h) {
   const TileLanes ln = tile_lanes(tl);
   const size_t row = static_cast<size_t>(a.leader) * g.N + ln.base + ln.lane;
   const float *mem = a.memory + row;
   const G *grads = static_cast<const G *>(a.grads) + row;
-  const uint32_t *keys_in = a.keys + ln.base + ln.lane;
   uint32_t key[kPerLane];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {   // all loads first
     key[c] = 0u;
-    if (slot_ok<kFull>(tl, ln, c)) key[c] = kFirst ? key_of(mem, grads, 64 * c) : keys_in[64 * c];
+    if (slot_ok<kFull>(tl, ln, c)) key[c] = key_of(mem, grads, 64 * c);
   }
   uint32_t *keys_out = a.keys + ln.base + ln.lane;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     if (!slot_ok<kFull>(tl, ln, c)) continue;
-    if (kFirst) keys_out[64 * c] = key[c];
-    if ((key[c] & hi_mask) == want) atomicAdd(&h[(key[c] >> shift) & (nb - 1)], 1u);
+    keys_out[64 * c] = key[c];
+    atomicAdd(&h[key[c] >> kShift0], 1u);
   }
 }
 
-// Histogram of digit (key >> shift) & (2^bits - 1) over the keys whose higher
-// digits equal the tensor's prefix so far.  The first pass (kFirst) computes
-// the keys from the leader's memory and gradient and stores them.
-template <typename G, bool kFirst>
-__global__ __launch_bounds__(kBlock) void topk_hist(Geometry g, TopkArgs a, int shift, int bits) {
+template <typename G>
+__global__ __launch_bounds__(kBlock) void topk_hist0(Geometry g, TopkArgs a) {
   __shared__ uint32_t h[kMaxBins];
-  const int nb = 1 << bits;
-  for (int i = threadIdx.x; i < nb; i += kBlock) h[i] = 0u;
+  for (int i = threadIdx.x; i < kMaxBins; i += kBlock) h[i] = 0u;
   __syncthreads();
   const Tile tl = g.tiles[blockIdx.x];
-  const uint32_t hi_mask = shift + bits >= 31 ? 0u : ~((1u << (shift + bits)) - 1u);
-  const uint32_t want = a.prefix[tl.tensor] & hi_mask;
   if (tl.len == kTile)
-    hist_tile<G, kFirst, true>(g, a, tl, h, shift, nb, hi_mask, want);
+    hist0_tile<G, true>(g, a, tl, h);
   else
-    hist_tile<G, kFirst, false>(g, a, tl, h, shift, nb, hi_mask, want);
+    hist0_tile<G, false>(g, a, tl, h);
   __syncthreads();
   uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
-  for (int i = threadIdx.x; i < nb; i += kBlock)
+  for (int i = threadIdx.x; i < kMaxBins; i += kBlock)
+    if (h[i]) atomicAdd(&out[i], h[i]);
+}
+
+// Pass 2: over the stored keys.  Keys above the first digit's bin b0 are
+// counted (tile_gt); keys in it are histogrammed by their next 11 bits and
+// written, compacted, to the tile's candidate list (tile_m of them).
+template <bool kFull>
+__device__ __forceinline__ void hist1_tile(const TopkArgs &a, const Tile &tl, uint32_t *h,
+                                           uint32_t *wcnt) {
+  const TileLanes ln = tile_lanes(tl);
+  const uint32_t b0 = a.prefix[tl.tensor] >> kShift0;
+  uint32_t key[kPerLane];
+  load_keys<kFull>(a, tl, ln, key);
+  uint32_t nm = 0, ngt = 0;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    const bool ok = slot_ok<kFull>(tl, ln, c);
+    const uint32_t d0 = key[c] >> kShift0;
+    nm += __popcll(__ballot(ok && d0 == b0));
+    ngt += __popcll(__ballot(ok && d0 > b0));
+  }
+  if (ln.lane == 0) {
+    wcnt[ln.wave] = nm;
+    wcnt[kWaves + ln.wave] = ngt;
+  }
+  __syncthreads();
+  uint32_t at = 0;   // this wavefront's first slot in the tile's candidate list
+  for (int v = 0; v < ln.wave; ++v) at += wcnt[v];
+  uint32_t *cand = a.cand + tl.start;
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c) {
+    const bool match = slot_ok<kFull>(tl, ln, c) && (key[c] >> kShift0) == b0;
+    const uint64_t bm = __ballot(match);
+    if (match) {
+      cand[at + __popcll(bm & lanemask_lt(ln.lane))] = key[c];
+      atomicAdd(&h[(key[c] >> kShift1) & (kMaxBins - 1)], 1u);
+    }
+    at += __popcll(bm);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void topk_hist1(Geometry g, TopkArgs a) {
+  __shared__ uint32_t h[kMaxBins];
+  __shared__ uint32_t wcnt[2 * kWaves];
+  for (int i = threadIdx.x; i < kMaxBins; i += kBlock) h[i] = 0u;
+  __syncthreads();
+  const Tile tl = g.tiles[blockIdx.x];
+  if (tl.len == kTile)
+    hist1_tile<true>(a, tl, h, wcnt);
+  else
+    hist1_tile<false>(a, tl, h, wcnt);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0, gt = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      m += wcnt[v];
+      gt += wcnt[kWaves + v];
+    }
+    a.tile_m[blockIdx.x] = m;
+    a.tile_gt[blockIdx.x] = gt;   // completed by topk_tile_counts
+    a.tile_eq[blockIdx.x] = 0u;
+  }
+  uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
+  for (int i = threadIdx.x; i < kMaxBins; i += kBlock)
+    if (h[i]) atomicAdd(&out[i], h[i]);
+}
+
+// Pass 3: the last 9 bits, over the candidates whose top 22 bits equal the
+// prefix.  A tile without candidates returns at once.
+__global__ __launch_bounds__(kBlock) void topk_hist2(Geometry g, TopkArgs a) {
+  __shared__ uint32_t h[512];
+  const uint32_t m = a.tile_m[blockIdx.x];
+  if (m == 0) return;   // uniform over the workgroup
+  const Tile tl = g.tiles[blockIdx.x];
+  const uint32_t want = a.prefix[tl.tensor] >> kShift1;
+  for (int i = threadIdx.x; i < 512; i += kBlock) h[i] = 0u;
+  __syncthreads();
+  const uint32_t *cand = a.cand + tl.start;
+  for (uint32_t j = threadIdx.x; j < m; j += kBlock) {
+    const uint32_t key = cand[j];
+    if ((key >> kShift1) == want) atomicAdd(&h[key & 511u], 1u);
+  }
+  __syncthreads();
+  uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
+  for (int i = threadIdx.x; i < 512; i += kBlock)
     if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
@@ -192,46 +286,25 @@ __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
   for (int j = 0; j < kPer; ++j) hist[b * kPer + j] = 0u;   // ready for the next pass
 }
 
-// The tile's stored keys, one per lane slot (0 past the tile's end).
-template <bool kFull>
-__device__ __forceinline__ void load_keys(const TopkArgs &a, const Tile &tl, const TileLanes &ln,
-                                          uint32_t (&key)[kPerLane]) {
-  const uint32_t *keys = a.keys + ln.base + ln.lane;
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    key[c] = 0u;
-    if (slot_ok<kFull>(tl, ln, c)) key[c] = keys[64 * c];
-  }
-}
-
 // ---------------------------------------------------------------------------
-// per-tile counts of keys above and at the threshold, then per-tensor offsets
+// per-tile counts above and at the threshold, then per-tensor offsets
 // ---------------------------------------------------------------------------
-template <bool kFull>
-__device__ __forceinline__ void count_tile(const TopkArgs &a, const Tile &tl, uint32_t tau,
-                                           uint32_t &gt, uint32_t &eq) {
-  const TileLanes ln = tile_lanes(tl);
-  uint32_t key[kPerLane];
-  load_keys<kFull>(a, tl, ln, key);
-  gt = 0;
-  eq = 0;
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    const bool ok = slot_ok<kFull>(tl, ln, c);
-    gt += __popcll(__ballot(ok && key[c] > tau));
-    eq += __popcll(__ballot(ok && key[c] == tau));
-  }
-}
-
-__global__ __launch_bounds__(kBlock) void topk_count(Geometry g, TopkArgs a) {
+// Keys above the first digit's bin were counted in pass 2; the candidates
+// give the rest.  A tile without candidates returns at once.
+__global__ __launch_bounds__(kBlock) void topk_tile_counts(Geometry g, TopkArgs a) {
   __shared__ uint32_t cnt[2][kWaves];
+  const uint32_t m = a.tile_m[blockIdx.x];
+  if (m == 0) return;   // uniform over the workgroup
   const Tile tl = g.tiles[blockIdx.x];
   const uint32_t tau = a.prefix[tl.tensor];
-  uint32_t gt, eq;
-  if (tl.len == kTile)
-    count_tile<true>(a, tl, tau, gt, eq);
-  else
-    count_tile<false>(a, tl, tau, gt, eq);
+  const uint32_t *cand = a.cand + tl.start;
+  uint32_t gt = 0, eq = 0;
+  for (uint32_t j0 = 0; j0 < m; j0 += kBlock) {   // uniform trip count: ballots stay converged
+    const uint32_t j = j0 + threadIdx.x;
+    const uint32_t key = j < m ? cand[j] : 0u;
+    gt += __popcll(__ballot(j < m && key > tau));
+    eq += __popcll(__ballot(j < m && key == tau));
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     cnt[0][wave] = gt;
@@ -244,7 +317,7 @@ __global__ __launch_bounds__(kBlock) void topk_count(Geometry g, TopkArgs a) {
       sg += cnt[0][v];
       se += cnt[1][v];
     }
-    a.tile_gt[blockIdx.x] = sg;
+    a.tile_gt[blockIdx.x] += sg;
     a.tile_eq[blockIdx.x] = se;
   }
 }
@@ -430,13 +503,13 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   const dim3 block(kBlock), tiles(g.num_tiles), tensors(g.T);
   hipLaunchKernelGGL(topk_reset, dim3(stride_grid(static_cast<int64_t>(g.T) * kMaxBins)), block, 0,
                      s, g, a);
-  hipLaunchKernelGGL((topk_hist<G, true>), tiles, block, 0, s, g, a, kShift0, 11);
+  hipLaunchKernelGGL(topk_hist0<G>, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift0);
-  hipLaunchKernelGGL((topk_hist<G, false>), tiles, block, 0, s, g, a, kShift1, 11);
+  hipLaunchKernelGGL(topk_hist1, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift1);
-  hipLaunchKernelGGL((topk_hist<G, false>), tiles, block, 0, s, g, a, kShift2, 9);
+  hipLaunchKernelGGL(topk_hist2, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<9>, tensors, block, 0, s, a, kShift2);
-  hipLaunchKernelGGL(topk_count, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL(topk_tile_counts, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);
 }
 

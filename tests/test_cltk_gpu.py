@@ -90,6 +90,22 @@ def test_cltk_ties_and_zeros():
     log(f"cltk ties: {exact}/{total}")
 
 
+def test_cltk_all_keys_equal():
+    """Every |x| equal (constant gradients, zero memories): every key is a
+    candidate and every selected entry is a tie, taken from the lowest index."""
+    wl = _wl("cltk_equal_w3", (70000, 8193, 64, 1), 3, steps=2)
+    off, N = padded_layout(wl.numel)
+
+    def grads_fn(k):
+        g = torch.zeros(wl.workers, N, device="cuda")
+        for w in range(wl.workers):
+            for t, n in enumerate(wl.numel):
+                g[w, off[t]: off[t] + n] = 0.25 * (w + 1) * (1 if k % 2 == 0 else -1)
+        return g
+    memory = torch.zeros(wl.workers, N, device="cuda")
+    _run(wl, 0.3, wl.steps, grads_fn=grads_fn, memory=memory)
+
+
 def test_cltk_configure_rejects_bad_density():
     from error_compensated_bit_02_amd import OneBitAdam, OneBitError
     ctx = OneBitAdam((100, 7), 2, "f32", 0.9, 1e-8)
