@@ -370,11 +370,43 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
 // threshold, or at it with tie rank < r; lane c of each wavefront keeps word
 // c of the mask and the position of its first selected entry.  The first
 // group writes the index list; every group then streams its workers.
+//
+// A tile's selected entries are one contiguous run of positions in each
+// worker's message, so the workgroup stages all its workers' entries in LDS
+// and writes them with one coalesced pass at the end: written directly, each
+// would be a 4-byte store into a line that many other stores also write.
+// When the run times the workers exceeds kStage entries the entries are
+// written directly (at such densities the direct stores are nearly dense).
 // ---------------------------------------------------------------------------
+constexpr int kStage = 4096;
+
+struct TileSelection {
+  uint64_t selw;     // lane c: word c of the wavefront's selection mask
+  int64_t posw;      // lane c: position of that word's first selected entry
+  int64_t first;     // position of the tile's first selected entry
+  int64_t count;     // selected entries in the tile
+};
+
+// The messages and the index list are written with non-temporal stores:
+// they are not read again by this exchange, and cached like the streamed
+// memories they cost the gather ~5% at BERT-Large (measured).
+__device__ __forceinline__ void store_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+
+// Copies stage[0 .. count) to out[first + j] for first + j < k_end.
+__device__ __forceinline__ void flush_stage(const uint32_t *stage, uint32_t *out, int64_t first,
+                                            int64_t count, int64_t k_end) {
+  __syncthreads();   // the staged entries are complete
+  for (int64_t j = threadIdx.x; j < count; j += kBlock)
+    if (first + j < k_end) store_nt(out + first + j, stage[j]);
+  __syncthreads();   // the stage may be refilled
+}
+
 template <bool kFull>
-__device__ __forceinline__ void select_words(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                             int tile, const TileLanes &ln, int64_t *wcnt,
-                                             bool write_index, uint64_t &selw, int64_t &posw) {
+__device__ __forceinline__ TileSelection select_words(const Geometry &g, const TopkArgs &a,
+                                                      const Tile &tl, int tile, const TileLanes &ln,
+                                                      int64_t *wcnt, uint32_t *stage,
+                                                      bool write_index) {
   const int t = tl.tensor;
   const uint32_t tau = a.prefix[t];
   const int64_t r = a.krem[t];
@@ -399,7 +431,8 @@ __device__ __forceinline__ void select_words(const Geometry &g, const TopkArgs &
   int64_t eq_run = a.tile_eq_before[tile];
   for (int v = 0; v < ln.wave; ++v) eq_run += wcnt[v];
   __syncthreads();   // wcnt is reused below
-  selw = 0;
+  TileSelection sel;
+  sel.selw = 0;
   int64_t nsel = 0;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
@@ -408,61 +441,93 @@ __device__ __forceinline__ void select_words(const Geometry &g, const TopkArgs &
     const int64_t rank = eq_run + __popcll(be & lanemask_lt(ln.lane));
     const bool take_eq = ((be >> ln.lane) & 1ull) && rank < r;
     const uint64_t bs = bg | __ballot(take_eq);
-    if (ln.lane == c) selw = bs;
+    if (ln.lane == c) sel.selw = bs;
     eq_run += __popcll(be);
     nsel += __popcll(bs);
   }
   if (ln.lane == 0) wcnt[ln.wave] = nsel;
   __syncthreads();
-  int64_t pos = a.tile_sel_off[tile];
-  for (int v = 0; v < ln.wave; ++v) pos += wcnt[v];
+  sel.first = a.tile_sel_off[tile];
+  sel.count = 0;
+  int64_t pos = sel.first;
+  for (int v = 0; v < kWaves; ++v) {
+    if (v < ln.wave) pos += wcnt[v];
+    sel.count += wcnt[v];
+  }
   // positions in ascending index order (index = position within the tensor)
   const int64_t tensor_start =
       tl.start - static_cast<int64_t>(tile - g.tile_begin[t]) * kTile;
   const int64_t k_end = a.k_off[t + 1];
-  posw = 0;
+  const bool staged = sel.count <= kStage;   // uniform over the workgroup
+  sel.posw = 0;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
-    const uint64_t bs = readlane64(selw, c);
-    if (ln.lane == c) posw = pos;
+    const uint64_t bs = readlane64(sel.selw, c);
+    if (ln.lane == c) sel.posw = pos;
     if (write_index && ((bs >> ln.lane) & 1ull)) {
       const int64_t at = pos + __popcll(bs & lanemask_lt(ln.lane));
-      if (at < k_end)   // always true when the selection holds k_t entries
-        a.index[at] = static_cast<int32_t>(ln.base + 64 * c + ln.lane - tensor_start);
+      const int32_t local = static_cast<int32_t>(ln.base + 64 * c + ln.lane - tensor_start);
+      if (staged)
+        stage[at - sel.first] = static_cast<uint32_t>(local);
+      else if (at < k_end)   // always true when the selection holds k_t entries
+        store_nt(reinterpret_cast<uint32_t *>(a.index) + at, static_cast<uint32_t>(local));
     }
     pos += __popcll(bs);
   }
+  if (write_index && staged && sel.count > 0)
+    flush_stage(stage, reinterpret_cast<uint32_t *>(a.index), sel.first, sel.count, k_end);
+  return sel;
 }
 
 template <typename G, bool kFull>
 __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                            int tile, int w_lo, int w_hi, int64_t *wcnt) {
+                                            int tile, int w_lo, int w_hi, int64_t *wcnt,
+                                            uint32_t *stage) {
   const TileLanes ln = tile_lanes(tl);
   const int64_t k_end = a.k_off[tl.tensor + 1];
-  uint64_t selw;
-  int64_t posw;
-  select_words<kFull>(g, a, tl, tile, ln, wcnt, w_lo == 0, selw, posw);
+  const TileSelection sel = select_words<kFull>(g, a, tl, tile, ln, wcnt, stage, w_lo == 0);
+  const int64_t staged_entries = sel.count * (w_hi - w_lo);
+  const bool staged = staged_entries <= kStage;   // uniform over the workgroup
   for (int w = w_lo; w < w_hi; ++w) {
     const size_t row = static_cast<size_t>(w) * g.N + ln.base + ln.lane;
     float *mem = a.memory + row;
     const G *gw = static_cast<const G *>(a.grads) + row;
     float *vals = a.values + static_cast<size_t>(w) * a.K;
+    uint32_t *wstage = stage + (w - w_lo) * sel.count;
     float x[kPerLane];
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {   // all loads first: the stores below may alias them
       x[c] = 0.0f;
       if (slot_ok<kFull>(tl, ln, c)) x[c] = mem[64 * c] + grad_at(gw + 64 * c);
     }
+    // The memory first, one full-row store per slot, in a loop of its own: in
+    // the same branch as the message's stores the compiler splits it into two
+    // half-masked stores (0 for the selected lanes, x for the others).
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
-      const uint64_t bs = readlane64(selw, c);
-      const bool mine = (bs >> ln.lane) & 1ull;   // never set past the tile's end
+      const bool mine = (readlane64(sel.selw, c) >> ln.lane) & 1ull;   // never set past the end
       if (slot_ok<kFull>(tl, ln, c)) mem[64 * c] = mine ? 0.0f : x[c];
-      if (mine) {
-        const int64_t at = static_cast<int64_t>(readlane64(static_cast<uint64_t>(posw), c)) +
+    }
+#pragma unroll
+    for (int c = 0; c < kPerLane; ++c) {
+      const uint64_t bs = readlane64(sel.selw, c);
+      if (bs == 0) continue;   // uniform: no entry of word c is selected
+      if ((bs >> ln.lane) & 1ull) {
+        const int64_t at = static_cast<int64_t>(readlane64(static_cast<uint64_t>(sel.posw), c)) +
                            __popcll(bs & lanemask_lt(ln.lane));
-        if (at < k_end) vals[at] = x[c];   // always true when the selection holds k_t entries
+        if (staged)
+          wstage[at - sel.first] = __float_as_uint(x[c]);
+        else if (at < k_end)   // always true when the selection holds k_t entries
+          store_nt(vals + at, x[c]);
       }
+    }
+  }
+  if (staged && staged_entries > 0) {
+    __syncthreads();   // every worker's entries are staged
+    for (int64_t e = threadIdx.x; e < staged_entries; e += kBlock) {
+      const int64_t wi = e / sel.count, j = e - wi * sel.count;
+      if (sel.first + j < k_end)
+        store_nt(a.values + static_cast<size_t>(w_lo + wi) * a.K + sel.first + j, __uint_as_float(stage[e]));
     }
   }
 }
@@ -470,15 +535,16 @@ __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a
 template <typename G>
 __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   __shared__ int64_t wcnt[kWaves];
+  __shared__ uint32_t stage[kStage];
   const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(g.num_tiles));
   const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(g.num_tiles));
   const int w_lo = grp * a.wgroup;
   const int w_hi = min(g.W, w_lo + a.wgroup);
   const Tile tl = g.tiles[tile];
   if (tl.len == kTile)
-    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt);
+    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt, stage);
   else
-    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt);
+    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt, stage);
 }
 
 // the server: average of the W messages, ascending workers from +0, then / W
