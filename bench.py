@@ -104,9 +104,9 @@ def counter_traffic(workload: str, kernel: str):
     return None if per is None else float(per)
 
 
-# rocprofv3 kernel names -> the library's kernel kinds.  The CLT-k select
-# stage is ten launches; its bytes are summed per exchange (per topk_reset).
-_SELECT_STAGE = ("topk_reset", "topk_hist", "topk_pick", "topk_count", "topk_offsets", "topk_select")
+# rocprofv3 kernel names -> the library's kernel kinds.  Every topk_ kernel
+# but the gather and the average belongs to the CLT-k select stage (nine
+# launches); its bytes are summed per exchange (per topk_reset).
 
 
 def kind_of(name: str):
@@ -122,12 +122,12 @@ def kind_of(name: str):
                 "server_residual")[int(args[0])]
     if base == "update_kernel":
         return "apply_update" if args[0] == "true" else "update_residual"
-    if base in _SELECT_STAGE:
-        return "cltk_select"
     if base == "topk_gather":
         return "cltk_gather"
     if base == "topk_average":
         return "cltk_average"
+    if base.startswith("topk_"):
+        return "cltk_select"
     return base
 
 
