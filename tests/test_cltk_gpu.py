@@ -127,3 +127,19 @@ def test_cltk_full_size_bert_large_sampled():
     idx = {n: i for i, (n, _) in enumerate(wl.tensors)}
     tensors = [idx[n] for n in ("layer0.attn.q.bias", "layer3.attn.v.weight", "embed.position")]
     _run(wl, 0.01, 3, tensors=tensors)
+
+
+def test_cltk_full_size_bert_base_w64_sampled():
+    """64 workers in groups of 16: every group rebuilds the selection; the
+    first writes the index list."""
+    wl = WORKLOADS["bert_base_w64"]
+    idx = {n: i for i, (n, _) in enumerate(wl.tensors)}
+    tensors = [idx[n] for n in ("layer0.attn.q.bias", "layer5.attn.k.weight", "layer11.ln2.beta")]
+    _run(wl, 0.01, 2, tensors=tensors)
+
+
+def test_cltk_full_size_gpt_1p3b_bf16_sampled():
+    wl = WORKLOADS["gpt_1p3b_bf16"]
+    idx = {n: i for i, (n, _) in enumerate(wl.tensors)}
+    tensors = [idx[n] for n in ("h0.ln1.gamma", "h0.attn.qkv.bias", "ln_f.beta")]
+    _run(wl, 0.01, 2, tensors=tensors)
