@@ -122,6 +122,8 @@ def kind_of(name: str):
                 "server_residual")[int(args[0])]
     if base == "update_kernel":
         return "apply_update" if args[0] == "true" else "update_residual"
+    if base.endswith("_kernel"):   # warmup, materialize, zero_errors, trust_norms, trust_ratio
+        return base[: -len("_kernel")]
     if base == "topk_gather":
         return "cltk_gather"
     if base == "topk_average":
@@ -270,6 +272,44 @@ def time_cltk(wl, ctx, grads, density, steps, warmup, stream):
     return dt, kernels
 
 
+def time_warmup_phase(wl, ctx, grads, steps, warmup, stream, beta2=0.999, lr=1e-3):
+    """Warmup, then `steps` timed steps of the uncompressed Adam warmup phase
+    (ob_warmup_step) from a fresh state.  Returns (seconds, kernels)."""
+    import torch
+    from synth import init_state
+    st = init_state(wl, "cuda")
+    sets = len(grads)
+    for k in range(warmup):
+        ctx.warmup_step(grads[k % sets], st["m"], st["v"], st["p"], beta2, lr, stream=stream)
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    ctx.profile_read(reset=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ctx.warmup_step(grads[(warmup + k) % sets], st["m"], st["v"], st["p"], beta2, lr, stream=stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kernels = ctx.profile_read(reset=True)
+    ctx.profile(False)
+    del st
+    return dt, kernels
+
+
+def summarize_warmup(wl, n_elem, steps, dt, kernels, workload):
+    """The warmup kernel reads g*W, m, v, p and writes m, v, p: 24 + g*W B/element."""
+    b = 24.0 + grad_bytes(wl) * wl.workers
+    ms, n = kernels["warmup"]
+    avg = ms / n
+    achieved = b * n_elem / (avg * 1e-3) / 1e9
+    traffic = counter_traffic(workload, "warmup")
+    return {"ms_per_step": dt * 1e3 / steps, "elements_per_s": n_elem * steps / dt,
+            "roofline": {"bound": "hbm", "kernel": "warmup", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                         "traffic": None if traffic is None else round(traffic),
+                         "bytes_per_element": b, "avg_ms": round(avg, 4)}}
+
+
 def summarize_cltk(wl, n_elem, steps, dt, kernels, density, workload):
     kb = cltk_bytes_per_element(wl, density)
     per = {k: (kernels[k][0] / kernels[k][1] if kernels[k][1] else 0.0) for k in kb}
@@ -369,6 +409,8 @@ def main() -> int:
                     help="layer-wise trust-ratio update with weight decay WD")
     ap.add_argument("--server-chunks", type=int, default=1,
                     help="partitioned server: one server scale per tensor chunk (1 = per tensor)")
+    ap.add_argument("--no-warmup-phase", action="store_true",
+                    help="skip timing the uncompressed Adam warmup phase")
     ap.add_argument("--cltk-density", type=float, default=0.01,
                     help="also time the cyclic local top-k exchange keeping this fraction of "
                          "each tensor (0 = skip)")
@@ -437,6 +479,14 @@ def main() -> int:
         log(f"bench: {form}: {results[form]['ms_per_step']:.3f} ms/step, "
             f"{100 * results[form]['step_frac_of_peak']:.1f}% of peak")
 
+    warm = None
+    if not args.no_warmup_phase:
+        torch.cuda.empty_cache()
+        dt, kernels = time_warmup_phase(wl, ctx, grads, args.steps, args.warmup, stream)
+        warm = summarize_warmup(wl, n_elem, args.steps, dt, kernels, wl.name)
+        log(f"bench: warmup-phase Adam: {warm['ms_per_step']:.3f} ms/step, "
+            f"{100 * warm['roofline']['frac']:.1f}% of peak")
+
     cltk = None
     if args.cltk_density > 0:
         torch.cuda.empty_cache()
@@ -466,6 +516,7 @@ def main() -> int:
     }
     if "strict" in results and forms[0] != "strict":
         result["strict_form"] = results["strict"]
+    result["warmup_phase"] = warm
     result["cltk"] = cltk
     torch.cuda.empty_cache()
     result["copy_ceiling"] = copy_ceiling()
