@@ -533,7 +533,8 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   const size_t nw = static_cast<size_t>(c->N / 64);
   const size_t sizes[] = {up((T + 1) * 8), up(T * 2048 * 4), up(T * 4),     up(T * 4),
                           up(tiles * 4),     up(tiles * 4),    up(tiles * 8), up(tiles * 8),
-                          up(nw * 64 * 4),   up(nw * 64 * 4),  up(tiles * 4)};
+                          up(nw * 64 * 4),   up(nw * 64 * 4),  up(tiles * 4), up(nw * 64 * 2),
+                          up(nw * 8)};
   size_t total = 0;
   for (size_t b : sizes) total += b;
   if (c->topk_scratch) {
@@ -564,6 +565,8 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   a.keys = reinterpret_cast<uint32_t *>(at[8]);
   a.cand = reinterpret_cast<uint32_t *>(at[9]);
   a.tile_m = reinterpret_cast<uint32_t *>(at[10]);
+  a.cand_pos = reinterpret_cast<uint16_t *>(at[11]);
+  a.above = reinterpret_cast<uint64_t *>(at[12]);
   a.K = k_off[T];
   if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess)
     return OB_ERR_DEVICE;

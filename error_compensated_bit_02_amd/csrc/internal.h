@@ -169,7 +169,9 @@ struct TopkArgs {
   uint32_t *prefix;          // [T] key prefix found so far, then the k-th largest key
   uint32_t *krem;            // [T] rank still to find, then the ties to take
   uint32_t *cand;            // [N] per tile, its keys in the first digit's bin, compacted
+  uint16_t *cand_pos;        // [N] their positions within the tile, ascending
   uint32_t *tile_m;          // [num_tiles] number of those keys
+  uint64_t *above;           // [Nw] bit per element: key above the first digit's bin
   uint32_t *tile_gt;         // [num_tiles] keys above the threshold
   uint32_t *tile_eq;         // [num_tiles] keys at the threshold
   int64_t *tile_eq_before;   // [num_tiles] keys at the threshold in earlier tiles of the tensor

@@ -14,10 +14,10 @@
 // per-tile counts at the threshold read only the candidates (a small fraction
 // of the keys unless many keys share the top 11 bits).  Ties at the threshold
 // go to the lowest indices; per-tensor scans give each tile its first
-// position.  Then one dense pass over all workers
-// rebuilds each tile's selection from the keys, writes the ascending index
-// list, gathers the messages and updates the memories, and the server
-// averages the W messages in ascending worker order.
+// position.  Then one dense pass over all workers rebuilds each tile's
+// selection from pass 2's mask of keys above the bin and its candidates,
+// writes the ascending index list, gathers the messages and updates the
+// memories, and the server averages the W messages in ascending worker order.
 //
 // The element mapping is the one of kernels.hip: a workgroup of 4
 // wavefronts owns a tile of up to kTile elements of one tensor, lane l of
@@ -166,13 +166,17 @@ __device__ __forceinline__ void hist1_tile(const TopkArgs &a, const Tile &tl, ui
   uint32_t key[kPerLane];
   load_keys<kFull>(a, tl, ln, key);
   uint32_t nm = 0, ngt = 0;
+  uint64_t gtw = 0;   // lane c: word c of the above-bin mask
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     const bool ok = slot_ok<kFull>(tl, ln, c);
     const uint32_t d0 = key[c] >> kShift0;
+    const uint64_t bg = __ballot(ok && d0 > b0);
+    if (ln.lane == c) gtw = bg;
     nm += __popcll(__ballot(ok && d0 == b0));
-    ngt += __popcll(__ballot(ok && d0 > b0));
+    ngt += __popcll(bg);
   }
+  if (ln.lane < ln.nwords) a.above[(ln.base >> 6) + ln.lane] = gtw;
   if (ln.lane == 0) {
     wcnt[ln.wave] = nm;
     wcnt[kWaves + ln.wave] = ngt;
@@ -181,12 +185,16 @@ __device__ __forceinline__ void hist1_tile(const TopkArgs &a, const Tile &tl, ui
   uint32_t at = 0;   // this wavefront's first slot in the tile's candidate list
   for (int v = 0; v < ln.wave; ++v) at += wcnt[v];
   uint32_t *cand = a.cand + tl.start;
+  uint16_t *cand_pos = a.cand_pos + tl.start;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     const bool match = slot_ok<kFull>(tl, ln, c) && (key[c] >> kShift0) == b0;
     const uint64_t bm = __ballot(match);
     if (match) {
-      cand[at + __popcll(bm & lanemask_lt(ln.lane))] = key[c];
+      // in ascending position order: wavefronts, then c, then lanes
+      const uint32_t slot = at + __popcll(bm & lanemask_lt(ln.lane));
+      cand[slot] = key[c];
+      cand_pos[slot] = static_cast<uint16_t>(ln.sub0 + 64 * c + ln.lane);
       atomicAdd(&h[(key[c] >> kShift1) & (kMaxBins - 1)], 1u);
     }
     at += __popcll(bm);
@@ -402,49 +410,52 @@ __device__ __forceinline__ void flush_stage(const uint32_t *stage, uint32_t *out
   __syncthreads();   // the stage may be refilled
 }
 
-template <bool kFull>
+// The tile's selection: keys above the first digit's bin (pass 2's mask), and
+// the candidates above the threshold or at it with tie rank < r.  The
+// candidates are in ascending position order, so a key at the threshold ranks
+// after tile_eq_before[tile] of them in earlier tiles and after those at the
+// threshold before it in the list.  Lane c of each wavefront then holds word c
+// of the mask and the position of its first selected entry.
 __device__ __forceinline__ TileSelection select_words(const Geometry &g, const TopkArgs &a,
                                                       const Tile &tl, int tile, const TileLanes &ln,
-                                                      int64_t *wcnt, uint32_t *stage,
-                                                      bool write_index) {
+                                                      int64_t *wcnt, uint64_t *smask,
+                                                      uint32_t *stage, bool write_index) {
   const int t = tl.tensor;
   const uint32_t tau = a.prefix[t];
   const int64_t r = a.krem[t];
-  uint32_t key[kPerLane];
-  load_keys<kFull>(a, tl, ln, key);
-  // keys at the threshold per wavefront; lane c keeps word c of each mask
-  uint64_t gtw = 0, eqw = 0;
-  int64_t neq = 0;
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    const bool ok = slot_ok<kFull>(tl, ln, c);
-    const uint64_t bg = __ballot(ok && key[c] > tau);
-    const uint64_t be = __ballot(ok && key[c] == tau);
-    if (ln.lane == c) {
-      gtw = bg;
-      eqw = be;
-    }
-    neq += __popcll(be);
-  }
-  if (ln.lane == 0) wcnt[ln.wave] = neq;
+  const int tile_words = (tl.len + 63) / 64;
+  for (int i = threadIdx.x; i < tile_words; i += kBlock) smask[i] = a.above[(tl.start >> 6) + i];
   __syncthreads();
+  const uint32_t m = a.tile_m[tile];   // uniform over the workgroup
+  const uint32_t *cand = a.cand + tl.start;
+  const uint16_t *cand_pos = a.cand_pos + tl.start;
   int64_t eq_run = a.tile_eq_before[tile];
-  for (int v = 0; v < ln.wave; ++v) eq_run += wcnt[v];
-  __syncthreads();   // wcnt is reused below
+  for (uint32_t j0 = 0; j0 < m; j0 += kBlock) {
+    const uint32_t j = j0 + threadIdx.x;
+    const bool valid = j < m;
+    const uint32_t key = valid ? cand[j] : 0u;
+    const bool at_tau = valid && key == tau;
+    const uint64_t be = __ballot(at_tau);
+    if (ln.lane == 0) wcnt[ln.wave] = __popcll(be);
+    __syncthreads();
+    int64_t before = 0, chunk = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      if (v < ln.wave) before += wcnt[v];
+      chunk += wcnt[v];
+    }
+    const int64_t rank = eq_run + before + __popcll(be & lanemask_lt(ln.lane));
+    if (valid && (key > tau || (at_tau && rank < r))) {
+      const uint32_t p = cand_pos[j];
+      atomicOr(reinterpret_cast<unsigned long long *>(&smask[p >> 6]), 1ull << (p & 63));
+    }
+    eq_run += chunk;
+    __syncthreads();   // wcnt and the mask words are complete
+  }
   TileSelection sel;
-  sel.selw = 0;
+  sel.selw = ln.lane < ln.nwords ? smask[ln.wave * kPerLane + ln.lane] : 0ull;
   int64_t nsel = 0;
 #pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    const uint64_t be = readlane64(eqw, c);
-    const uint64_t bg = readlane64(gtw, c);
-    const int64_t rank = eq_run + __popcll(be & lanemask_lt(ln.lane));
-    const bool take_eq = ((be >> ln.lane) & 1ull) && rank < r;
-    const uint64_t bs = bg | __ballot(take_eq);
-    if (ln.lane == c) sel.selw = bs;
-    eq_run += __popcll(be);
-    nsel += __popcll(bs);
-  }
+  for (int c = 0; c < kPerLane; ++c) nsel += __popcll(readlane64(sel.selw, c));
   if (ln.lane == 0) wcnt[ln.wave] = nsel;
   __syncthreads();
   sel.first = a.tile_sel_off[tile];
@@ -482,10 +493,10 @@ __device__ __forceinline__ TileSelection select_words(const Geometry &g, const T
 template <typename G, bool kFull>
 __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
                                             int tile, int w_lo, int w_hi, int64_t *wcnt,
-                                            uint32_t *stage) {
+                                            uint64_t *smask, uint32_t *stage) {
   const TileLanes ln = tile_lanes(tl);
   const int64_t k_end = a.k_off[tl.tensor + 1];
-  const TileSelection sel = select_words<kFull>(g, a, tl, tile, ln, wcnt, stage, w_lo == 0);
+  const TileSelection sel = select_words(g, a, tl, tile, ln, wcnt, smask, stage, w_lo == 0);
   const int64_t staged_entries = sel.count * (w_hi - w_lo);
   const bool staged = staged_entries <= kStage;   // uniform over the workgroup
   for (int w = w_lo; w < w_hi; ++w) {
@@ -535,6 +546,7 @@ __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a
 template <typename G>
 __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   __shared__ int64_t wcnt[kWaves];
+  __shared__ uint64_t smask[kTile / 64];
   __shared__ uint32_t stage[kStage];
   const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(g.num_tiles));
   const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(g.num_tiles));
@@ -542,9 +554,9 @@ __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   const int w_hi = min(g.W, w_lo + a.wgroup);
   const Tile tl = g.tiles[tile];
   if (tl.len == kTile)
-    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt, stage);
+    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt, smask, stage);
   else
-    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt, stage);
+    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt, smask, stage);
 }
 
 // the server: average of the W messages, ascending workers from +0, then / W
