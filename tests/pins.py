@@ -509,6 +509,24 @@ def pin_trust_ratio_update():
                           ob.preconditioned_update(ones, m1, v1, 0.1, 0.0))
 
 
+def pin_golden_cltk():
+    """Hand-derived two-exchange example (tests/golden/cltk_worked.txt): ties at
+    the boundary in both steps, the leader cycling from worker 0 to worker 1."""
+    g = load("cltk_worked.txt")
+    k = ints(g["k"])[0]
+    f = lambda key: np.array(floats(g[key]), dtype=np.float32)  # noqa: E731
+    mem = np.zeros((3, 6), np.float32)
+    for step in (0, 1):
+        grads = np.stack([f(f"step{step}.g{w}") for w in range(3)])
+        out = ob.cltk_step(mem, grads, step, k)
+        assert out.index.tolist() == ints(g[f"step{step}.index"]), step
+        for w in range(3):
+            assert out.values[w].tolist() == floats(g[f"step{step}.values{w}"]), (step, w)
+            assert out.memory[w].tolist() == floats(g[f"step{step}.mem{w}"]), (step, w)
+        assert out.average.tolist() == floats(g[f"step{step}.average"]), step
+        mem = out.memory
+
+
 def pin_cltk_brute_force():
     """Top-k positions by a pure-Python sort of (|x|, -index), ties included."""
     rng = _rng(21)

@@ -143,3 +143,29 @@ def test_cltk_full_size_gpt_1p3b_bf16_sampled():
     idx = {n: i for i, (n, _) in enumerate(wl.tensors)}
     tensors = [idx[n] for n in ("h0.ln1.gamma", "h0.attn.qkv.bias", "ln_f.beta")]
     _run(wl, 0.01, 2, tensors=tensors)
+
+
+def test_cltk_golden_worked_example():
+    """The hand-derived example of tests/golden/cltk_worked.txt through the C ABI:
+    the GPU must reproduce the hand values exactly (density 0.3: k = 2 of 6)."""
+    from error_compensated_bit_02_amd import OneBitAdam
+    from golden_io import floats, ints, load
+    g = load("cltk_worked.txt")
+    ctx = OneBitAdam([6], 3, "f32", 0.9, 1e-8)
+    assert ctx.cltk_configure(0.3) == [0, 2]
+    memory = torch.zeros(3, 64, device="cuda")
+    index = torch.zeros(2, dtype=torch.int32, device="cuda")
+    values = torch.zeros(3, 2, device="cuda")
+    average = torch.zeros(2, device="cuda")
+    for step in (0, 1):
+        grads = torch.zeros(3, 64, device="cuda")
+        for w in range(3):
+            grads[w, :6] = torch.tensor(floats(g[f"step{step}.g{w}"]))
+        ctx.cltk_step(step, grads, memory, index, values, average)
+        torch.cuda.synchronize()
+        assert index.cpu().tolist() == ints(g[f"step{step}.index"]), step
+        for w in range(3):
+            assert values[w].cpu().tolist() == floats(g[f"step{step}.values{w}"]), (step, w)
+            assert memory[w, :6].cpu().tolist() == floats(g[f"step{step}.mem{w}"]), (step, w)
+        assert average.cpu().tolist() == floats(g[f"step{step}.average"]), step
+    ctx.close()
