@@ -122,12 +122,13 @@ int ob_compress_worker(ob_ctx *ctx, int32_t w_begin, int32_t w_end, const void *
 /* Server: decompress and average all W messages, add the server error,
  * re-compress, store the new server error.
  *   packed_w [W][Nw], scale_w [W][T] read; err_s [N] read and overwritten;
- *   packed_s [Nw] and scale_s [T] written (the server message). */
+ *   packed_s [Nw] and scale_s [S] written (the server message; S = T unless the
+ *   server is partitioned, see ob_set_server_chunks). */
 int ob_server_reduce(ob_ctx *ctx, const uint64_t *packed_w, const float *scale_w,
                      float *err_s, uint64_t *packed_s, float *scale_s, void *stream);
 
 /* Update from the server message with the frozen variance:
- *   packed_s [Nw], scale_s [T], v [N] read; m [N] written; params [N] read and
+ *   packed_s [Nw], scale_s [S], v [N] read; m [N] written; params [N] read and
  *   overwritten.  lr must be finite. */
 int ob_apply_update(ob_ctx *ctx, const uint64_t *packed_s, const float *scale_s,
                     const float *v, float *m, float *params, double lr, void *stream);
@@ -167,7 +168,7 @@ int ob_step_residual(ob_ctx *ctx, int32_t first, const void *grads, const float 
 /* Writes the strict-form state of a residual-form state:
  *   err_w [W][N] = x_w - s_w,t*sign(x_w),  err_s [N] = z - s_s,t*sign(z),
  *   m [N] = s_s,t*sign(z).
- * x_w [W][N], scale_w [W][T], z [N], scale_s [T] are read.  Outputs may be
+ * x_w [W][N], scale_w [W][T], z [N], scale_s [S] are read.  Outputs may be
  * the same buffers as the inputs (in place). */
 int ob_materialize(ob_ctx *ctx, const float *x_w, const float *scale_w, const float *z,
                    const float *scale_s, float *err_w, float *err_s, float *m, void *stream);
