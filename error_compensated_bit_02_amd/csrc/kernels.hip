@@ -234,8 +234,11 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
       dd_accumulate(hi, lo, x);  // lanes outside the tile hold x = 0 and add nothing
       if (kMode != kPass1 && ok) ew[64 * c] = x;
     }
+    // Non-temporal: the sign words are read only by the server pass.  Cached,
+    // one 256-byte row piece per worker beside the x rows slowed this pass by
+    // ~7% at W = 64 (measured; no effect at W = 8).
     if (ln.lane < ln.nwords)
-      a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane] = word;
+      __builtin_nontemporal_store(word, &a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane]);
     const int slot = (w - w_lo) % kFlushRows;
     park_partial(sink, slot, ln.wave, hi, lo);
     if (slot == kFlushRows - 1 || w == w_hi - 1) flush_partials(sink, w - slot, slot + 1);
