@@ -73,6 +73,15 @@ def test_many_workers_w64_correlated():
     _report(wl.name, rep)
 
 
+@pytest.mark.parametrize("residual", [False, True], ids=["strict", "residual"])
+def test_many_workers_w200(residual):
+    """W = 200 (not a power of two): worker groups of up to 16, the server's
+    word loads in groups of 8 with a ragged last group, 201 partial-sum rows."""
+    wl = _wl("w200", (1, 65, 8193, 20000), 200, steps=2)
+    rep = parity_run(wl, wl.steps, residual=residual)
+    _report(wl.name, rep)
+
+
 def test_split_calls_equal_oracle():
     wl = _wl("ragged_split_w5", RAGGED, 5, steps=3)
     rep = parity_run(wl, wl.steps, split=True)
