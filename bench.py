@@ -332,7 +332,7 @@ def summarize_cltk(wl, n_elem, steps, dt, kernels, density, workload):
 
 def copy_ceiling(gib: int = 4, reps: int = 5) -> dict:
     """A plain device-to-device copy of `gib` GiB, timed with events on torch's
-    stream: the streaming rate a read+write kernel can reach on this machine."""
+    stream: the streaming rate a read+write kernel can reach on this device."""
     import torch
     n = gib << 28                      # fp32 elements
     src = torch.ones(n, device="cuda")
@@ -434,7 +434,7 @@ def main() -> int:
             log(f"  {k:24s} {v / 1e9:9.3f} GB per launch")
         return 0
     if args.gpus != 1:
-        log(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "
+        log(f"bench.py: --gpus {args.gpus} is not supported; this library runs on one GPU "
             f"(all W simulated workers share one GPU's HBM)")
         return 2
 

@@ -24,7 +24,7 @@ def _device():
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
     from error_compensated_bit_02_amd import load_library
-    load_library()          # a missing library is an error on a GPU machine, not a skip
+    load_library()          # with a GPU present, a missing library is an error, not a skip
     yield
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
