@@ -48,7 +48,9 @@
  * counts (allocated in ob_cltk_configure); ob_destroy frees both.
  *
  * Streams.  Every device call enqueues its kernels on the given stream (a
- * hipStream_t; NULL means the null stream) and returns without waiting.
+ * hipStream_t; NULL means the null stream) and returns without waiting.  A
+ * context's scratch lives on the device that was current at ob_init: later
+ * calls must pass buffers and a stream of that device, with it current.
  * Results are visible to later work on that stream.  Concurrent calls on one
  * context from several host threads, or on several streams at once, race on
  * the context's scratch and are not allowed.
