@@ -533,8 +533,8 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   const size_t nw = static_cast<size_t>(c->N / 64);
   const size_t sizes[] = {up((T + 1) * 8), up(T * 2048 * 4), up(T * 4),     up(T * 4),
                           up(tiles * 4),     up(tiles * 4),    up(tiles * 8), up(tiles * 8),
-                          up(nw * 64 * 4),   up(nw * 64 * 4),  up(tiles * 4), up(nw * 64 * 2),
-                          up(nw * 8)};
+                          up(T * 4),         up(nw * 64 * 4),  up(tiles * 4), up(nw * 64 * 2),
+                          up(nw * 8),        up(T * 4)};
   size_t total = 0;
   for (size_t b : sizes) total += b;
   if (c->topk_scratch) {
@@ -562,13 +562,16 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   a.tile_eq = reinterpret_cast<uint32_t *>(at[5]);
   a.tile_eq_before = reinterpret_cast<int64_t *>(at[6]);
   a.tile_sel_off = reinterpret_cast<int64_t *>(at[7]);
-  a.keys = reinterpret_cast<uint32_t *>(at[8]);
+  a.pred = reinterpret_cast<uint32_t *>(at[8]);
   a.cand = reinterpret_cast<uint32_t *>(at[9]);
   a.tile_m = reinterpret_cast<uint32_t *>(at[10]);
   a.cand_pos = reinterpret_cast<uint16_t *>(at[11]);
   a.above = reinterpret_cast<uint64_t *>(at[12]);
+  a.miss = reinterpret_cast<uint32_t *>(at[13]);
   a.K = k_off[T];
-  if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess)
+  const std::vector<uint32_t> no_prediction(T, 0xffffffffu);   // the first exchange has none
+  if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(at[8], no_prediction.data(), T * 4, hipMemcpyHostToDevice) != hipSuccess)
     return OB_ERR_DEVICE;
   c->k_off = k_off;
   if (k_total) *k_total = a.K;

@@ -164,14 +164,15 @@ struct TopkArgs {
   float *average;            // [K] the server's average
   int64_t K;                 // total entries over the tensor list
   const int64_t *k_off;      // [T+1] tensor t's entries are k_off[t] .. k_off[t+1]-1
-  uint32_t *keys;            // [N] the leader's keys, bit patterns of |memory + grads|
   uint32_t *hist;            // [T][2048] radix histograms
   uint32_t *prefix;          // [T] key prefix found so far, then the k-th largest key
   uint32_t *krem;            // [T] rank still to find, then the ties to take
-  uint32_t *cand;            // [N] per tile, its keys in the first digit's bin, compacted
+  uint32_t *cand;            // [N] per tile, its keys inside the first-digit window, compacted
   uint16_t *cand_pos;        // [N] their positions within the tile, ascending
   uint32_t *tile_m;          // [num_tiles] number of those keys
-  uint64_t *above;           // [Nw] bit per element: key above the first digit's bin
+  uint64_t *above;           // [Nw] bit per element: key above the window
+  uint32_t *pred;            // [T] first digit of the last threshold (the window's centre); kept
+  uint32_t *miss;            // [T] 1 when this exchange's first digit fell outside the window
   uint32_t *tile_gt;         // [num_tiles] keys above the threshold
   uint32_t *tile_eq;         // [num_tiles] keys at the threshold
   int64_t *tile_eq_before;   // [num_tiles] keys at the threshold in earlier tiles of the tensor

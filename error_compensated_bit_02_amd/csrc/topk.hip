@@ -6,18 +6,20 @@
 // Per tensor, the leader worker (step mod W) ranks |x_leader| = |mem + g|
 // and every worker sends its x at the leader's k largest positions.  The
 // selection is exact: the k-th largest key (the bit pattern of |x|, which
-// orders non-negative floats) is found by a 3-pass radix select with 11, 11
-// and 9-bit digits (per-tile LDS histograms added into per-tensor
-// histograms).  The first pass stores the keys; the second reads them,
-// counts per tile the keys above the first digit's bin and compacts the
-// tile's keys inside that bin into a candidate list; the third pass and the
-// per-tile counts at the threshold read only the candidates (a small fraction
-// of the keys unless many keys share the top 11 bits).  Ties at the threshold
-// go to the lowest indices; per-tensor scans give each tile its first
-// position.  Then one dense pass over all workers rebuilds each tile's
-// selection from pass 2's mask of keys above the bin and its candidates,
-// writes the ascending index list, gathers the messages and updates the
-// memories, and the server averages the W messages in ascending worker order.
+// orders non-negative floats) is found by a radix select with 11, 11 and
+// 9-bit digits (per-tile LDS histograms added into per-tensor histograms).
+// Pass 1 reads the leader's memory and gradient once: the first digit's
+// histogram, and for a window of first-digit bins around the previous
+// exchange's threshold, per tile, a bit mask of the keys above the window and
+// the keys inside it (the candidates) with their positions.  If the
+// threshold's first digit falls outside the window (or at the first
+// exchange), a fallback pass rebuilds that data for the tensor.  The later
+// digits and the per-tile counts read only the candidates.  Ties at the
+// threshold go to the lowest indices; per-tensor scans give each tile its
+// first position.  Then one dense pass over all workers rebuilds each tile's
+// selection from the mask and the candidates, writes the ascending index
+// list, gathers the messages and updates the memories, and the server
+// averages the W messages in ascending worker order.
 //
 // The element mapping is the one of kernels.hip: a workgroup of 4
 // wavefronts owns a tile of up to kTile elements of one tensor, lane l of
@@ -83,9 +85,22 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
 
 // ---------------------------------------------------------------------------
 // radix select over the 31-bit keys: digits of 11, 11 and 9 bits
+//
+// Pass 1 reads the leader's memory and gradient once.  Besides the histogram
+// of the top 11 bits (digit 0) it prepares, per tile, the input of every
+// later step for a window of digit-0 bins around the bin the threshold fell
+// in at the previous exchange: a bit per element for keys above the window,
+// their count, and the keys inside the window with their positions,
+// compacted (the candidates).  Once digit 0 of the threshold is known, a
+// tensor whose bin lies in the window needs nothing more from the dense
+// data; for the others (and at the first exchange) a fallback pass rebuilds
+// the same per-tile data for the window [b0, b0].  Candidates from other
+// window bins never tie with the threshold: they compare above or below it.
 // ---------------------------------------------------------------------------
 constexpr int kMaxBins = 2048;
 constexpr int kShift0 = 20, kShift1 = 9, kShift2 = 0;
+constexpr uint32_t kNoBin = 0xffffffffu;     // no prediction yet
+constexpr uint32_t kWindowBelow = 2, kWindowAbove = 4;   // the threshold's bin drifts upward
 
 // Grid-stride launches (grid capped at kStrideBlocks) for the two kernels
 // whose size is not a tile count.
@@ -103,77 +118,50 @@ __global__ __launch_bounds__(kBlock) void topk_reset(Geometry g, TopkArgs a) {
   }
 }
 
-// The tile's stored keys, one per lane slot (0 past the tile's end).
-template <bool kFull>
-__device__ __forceinline__ void load_keys(const TopkArgs &a, const Tile &tl, const TileLanes &ln,
-                                          uint32_t (&key)[kPerLane]) {
-  const uint32_t *keys = a.keys + ln.base + ln.lane;
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    key[c] = 0u;
-    if (slot_ok<kFull>(tl, ln, c)) key[c] = keys[64 * c];
-  }
+// Digit-0 window [lo, hi] of tensor t for this exchange's pass 1; lo > hi
+// when there is no prediction.
+struct Window {
+  uint32_t lo, hi;
+};
+
+__device__ __forceinline__ Window predicted_window(const TopkArgs &a, int t) {
+  const uint32_t b = a.pred[t];
+  if (b == kNoBin) return Window{1u, 0u};
+  return Window{b >= kWindowBelow ? b - kWindowBelow : 0u,
+                b + kWindowAbove < kMaxBins ? b + kWindowAbove : kMaxBins - 1u};
 }
 
-// Pass 1: the keys from the leader's memory and gradient, stored, and the
-// histogram of their top 11 bits.
+// The tile's keys, from the leader's memory and gradient (0 past the end).
 template <typename G, bool kFull>
-__device__ __forceinline__ void hist0_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                           uint32_t *h) {
-  const TileLanes ln = tile_lanes(tl);
+__device__ __forceinline__ void leader_keys(const Geometry &g, const TopkArgs &a, const Tile &tl,
+                                            const TileLanes &ln, uint32_t (&key)[kPerLane]) {
   const size_t row = static_cast<size_t>(a.leader) * g.N + ln.base + ln.lane;
   const float *mem = a.memory + row;
   const G *grads = static_cast<const G *>(a.grads) + row;
-  uint32_t key[kPerLane];
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {   // all loads first
     key[c] = 0u;
     if (slot_ok<kFull>(tl, ln, c)) key[c] = key_of(mem, grads, 64 * c);
   }
-  uint32_t *keys_out = a.keys + ln.base + ln.lane;
-#pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    if (!slot_ok<kFull>(tl, ln, c)) continue;
-    keys_out[64 * c] = key[c];
-    atomicAdd(&h[key[c] >> kShift0], 1u);
-  }
 }
 
-template <typename G>
-__global__ __launch_bounds__(kBlock) void topk_hist0(Geometry g, TopkArgs a) {
-  __shared__ uint32_t h[kMaxBins];
-  for (int i = threadIdx.x; i < kMaxBins; i += kBlock) h[i] = 0u;
-  __syncthreads();
-  const Tile tl = g.tiles[blockIdx.x];
-  if (tl.len == kTile)
-    hist0_tile<G, true>(g, a, tl, h);
-  else
-    hist0_tile<G, false>(g, a, tl, h);
-  __syncthreads();
-  uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
-  for (int i = threadIdx.x; i < kMaxBins; i += kBlock)
-    if (h[i]) atomicAdd(&out[i], h[i]);
-}
-
-// Pass 2: over the stored keys.  Keys above the first digit's bin b0 are
-// counted (tile_gt); keys in it are histogrammed by their next 11 bits and
-// written, compacted, to the tile's candidate list (tile_m of them).
+// Per tile, for the digit-0 window [w.lo, w.hi]: the bit mask of keys above
+// it (a.above), their count (tile_gt), and the keys inside it with their
+// positions, compacted in ascending position order (cand, cand_pos, tile_m).
+// Workgroup-uniform call; wcnt holds 2 * kWaves counters.
 template <bool kFull>
-__device__ __forceinline__ void hist1_tile(const TopkArgs &a, const Tile &tl, uint32_t *h,
-                                           uint32_t *wcnt) {
-  const TileLanes ln = tile_lanes(tl);
-  const uint32_t b0 = a.prefix[tl.tensor] >> kShift0;
-  uint32_t key[kPerLane];
-  load_keys<kFull>(a, tl, ln, key);
+__device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, const TileLanes &ln,
+                                            const uint32_t (&key)[kPerLane], Window w,
+                                            uint32_t *wcnt) {
   uint32_t nm = 0, ngt = 0;
-  uint64_t gtw = 0;   // lane c: word c of the above-bin mask
+  uint64_t gtw = 0;   // lane c: word c of the above-window mask
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     const bool ok = slot_ok<kFull>(tl, ln, c);
     const uint32_t d0 = key[c] >> kShift0;
-    const uint64_t bg = __ballot(ok && d0 > b0);
+    const uint64_t bg = __ballot(ok && d0 > w.hi);
     if (ln.lane == c) gtw = bg;
-    nm += __popcll(__ballot(ok && d0 == b0));
+    nm += __popcll(__ballot(ok && d0 >= w.lo && d0 <= w.hi));
     ngt += __popcll(bg);
   }
   if (ln.lane < ln.nwords) a.above[(ln.base >> 6) + ln.lane] = gtw;
@@ -188,29 +176,17 @@ __device__ __forceinline__ void hist1_tile(const TopkArgs &a, const Tile &tl, ui
   uint16_t *cand_pos = a.cand_pos + tl.start;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
-    const bool match = slot_ok<kFull>(tl, ln, c) && (key[c] >> kShift0) == b0;
+    const uint32_t d0 = key[c] >> kShift0;
+    const bool match = slot_ok<kFull>(tl, ln, c) && d0 >= w.lo && d0 <= w.hi;
     const uint64_t bm = __ballot(match);
     if (match) {
       // in ascending position order: wavefronts, then c, then lanes
       const uint32_t slot = at + __popcll(bm & lanemask_lt(ln.lane));
       cand[slot] = key[c];
       cand_pos[slot] = static_cast<uint16_t>(ln.sub0 + 64 * c + ln.lane);
-      atomicAdd(&h[(key[c] >> kShift1) & (kMaxBins - 1)], 1u);
     }
     at += __popcll(bm);
   }
-}
-
-__global__ __launch_bounds__(kBlock) void topk_hist1(Geometry g, TopkArgs a) {
-  __shared__ uint32_t h[kMaxBins];
-  __shared__ uint32_t wcnt[2 * kWaves];
-  for (int i = threadIdx.x; i < kMaxBins; i += kBlock) h[i] = 0u;
-  __syncthreads();
-  const Tile tl = g.tiles[blockIdx.x];
-  if (tl.len == kTile)
-    hist1_tile<true>(a, tl, h, wcnt);
-  else
-    hist1_tile<false>(a, tl, h, wcnt);
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t m = 0, gt = 0;
@@ -222,29 +198,92 @@ __global__ __launch_bounds__(kBlock) void topk_hist1(Geometry g, TopkArgs a) {
     a.tile_gt[blockIdx.x] = gt;   // completed by topk_tile_counts
     a.tile_eq[blockIdx.x] = 0u;
   }
+}
+
+// Pass 1: digit-0 histogram of the leader's keys, and the per-tile data for
+// the predicted window (none at the first exchange).
+template <typename G>
+__global__ __launch_bounds__(kBlock) void topk_pass1(Geometry g, TopkArgs a) {
+  __shared__ uint32_t h[kMaxBins];
+  __shared__ uint32_t wcnt[2 * kWaves];
+  for (int i = threadIdx.x; i < kMaxBins; i += kBlock) h[i] = 0u;
+  __syncthreads();
+  const Tile tl = g.tiles[blockIdx.x];
+  const TileLanes ln = tile_lanes(tl);
+  const Window w = predicted_window(a, tl.tensor);
+  uint32_t key[kPerLane];
+  if (tl.len == kTile)
+    leader_keys<G, true>(g, a, tl, ln, key);
+  else
+    leader_keys<G, false>(g, a, tl, ln, key);
+#pragma unroll
+  for (int c = 0; c < kPerLane; ++c)
+    if (ln.sub0 + 64 * c + ln.lane < tl.len) atomicAdd(&h[key[c] >> kShift0], 1u);
+  if (w.lo <= w.hi) {   // uniform over the workgroup
+    if (tl.len == kTile)
+      window_tile<true>(a, tl, ln, key, w, wcnt);
+    else
+      window_tile<false>(a, tl, ln, key, w, wcnt);
+  }
+  __syncthreads();
   uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
   for (int i = threadIdx.x; i < kMaxBins; i += kBlock)
     if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
-// Pass 3: the last 9 bits, over the candidates whose top 22 bits equal the
-// prefix.  A tile without candidates returns at once.
-__global__ __launch_bounds__(kBlock) void topk_hist2(Geometry g, TopkArgs a) {
-  __shared__ uint32_t h[512];
+// After digit 0 is known: whether it fell in the predicted window (if not,
+// the fallback pass rebuilds the tensor's per-tile data), and the prediction
+// for the next exchange.
+__global__ __launch_bounds__(kBlock) void topk_check(Geometry g, TopkArgs a) {
+  const int t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= g.T) return;
+  const Window w = predicted_window(a, t);
+  const uint32_t b0 = a.prefix[t] >> kShift0;
+  a.miss[t] = (w.lo <= w.hi && b0 >= w.lo && b0 <= w.hi) ? 0u : 1u;
+  a.pred[t] = b0;
+}
+
+// Fallback: for the tensors whose digit 0 missed the window, the per-tile
+// data for the window [b0, b0], from the leader's memory and gradient again.
+template <typename G>
+__global__ __launch_bounds__(kBlock) void topk_refill(Geometry g, TopkArgs a) {
+  __shared__ uint32_t wcnt[2 * kWaves];
+  const Tile tl = g.tiles[blockIdx.x];
+  if (a.miss[tl.tensor] == 0u) return;   // uniform over the workgroup
+  const TileLanes ln = tile_lanes(tl);
+  const uint32_t b0 = a.prefix[tl.tensor] >> kShift0;
+  uint32_t key[kPerLane];
+  if (tl.len == kTile) {
+    leader_keys<G, true>(g, a, tl, ln, key);
+    window_tile<true>(a, tl, ln, key, Window{b0, b0}, wcnt);
+  } else {
+    leader_keys<G, false>(g, a, tl, ln, key);
+    window_tile<false>(a, tl, ln, key, Window{b0, b0}, wcnt);
+  }
+}
+
+// Digits 1 and 2 over the candidates only: the histogram of
+// (key >> kShiftD) & (2^kBits - 1) over the candidates whose higher bits equal
+// the prefix found so far.  A tile without candidates returns at once.
+template <int kShiftD, int kBits>
+__global__ __launch_bounds__(kBlock) void topk_hist_cand(Geometry g, TopkArgs a) {
+  constexpr int kBins = 1 << kBits;
+  constexpr int kHigh = kShiftD + kBits;   // bits above this digit are fixed
+  __shared__ uint32_t h[kBins];
   const uint32_t m = a.tile_m[blockIdx.x];
   if (m == 0) return;   // uniform over the workgroup
   const Tile tl = g.tiles[blockIdx.x];
-  const uint32_t want = a.prefix[tl.tensor] >> kShift1;
-  for (int i = threadIdx.x; i < 512; i += kBlock) h[i] = 0u;
+  const uint32_t want = a.prefix[tl.tensor] >> kHigh;
+  for (int i = threadIdx.x; i < kBins; i += kBlock) h[i] = 0u;
   __syncthreads();
   const uint32_t *cand = a.cand + tl.start;
   for (uint32_t j = threadIdx.x; j < m; j += kBlock) {
     const uint32_t key = cand[j];
-    if ((key >> kShift1) == want) atomicAdd(&h[key & 511u], 1u);
+    if ((key >> kHigh) == want) atomicAdd(&h[(key >> kShiftD) & (kBins - 1)], 1u);
   }
   __syncthreads();
   uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
-  for (int i = threadIdx.x; i < 512; i += kBlock)
+  for (int i = threadIdx.x; i < kBins; i += kBlock)
     if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
@@ -297,7 +336,7 @@ __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
 // ---------------------------------------------------------------------------
 // per-tile counts above and at the threshold, then per-tensor offsets
 // ---------------------------------------------------------------------------
-// Keys above the first digit's bin were counted in pass 2; the candidates
+// Keys above the window were counted with the candidates; the candidates
 // give the rest.  A tile without candidates returns at once.
 __global__ __launch_bounds__(kBlock) void topk_tile_counts(Geometry g, TopkArgs a) {
   __shared__ uint32_t cnt[2][kWaves];
@@ -373,11 +412,12 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // selection and gather.  Workgroups are (worker group, tile), group-major as
-// in the worker passes.  Each rebuilds its tile's selection from the stored
-// keys (read-only here, so groups need no ordering): selected = key above the
-// threshold, or at it with tie rank < r; lane c of each wavefront keeps word
-// c of the mask and the position of its first selected entry.  The first
-// group writes the index list; every group then streams its workers.
+// in the worker passes.  Each rebuilds its tile's selection from the mask of
+// keys above the window and the candidates (read-only here, so groups need
+// no ordering): selected = key above the threshold, or at it with tie rank
+// < r; lane c of each wavefront keeps word c of the mask and the position of
+// its first selected entry.  The first group writes the index list; every
+// group then streams its workers.
 //
 // A tile's selected entries are one contiguous run of positions in each
 // worker's message, so the workgroup stages all its workers' entries in LDS
@@ -410,8 +450,8 @@ __device__ __forceinline__ void flush_stage(const uint32_t *stage, uint32_t *out
   __syncthreads();   // the stage may be refilled
 }
 
-// The tile's selection: keys above the first digit's bin (pass 2's mask), and
-// the candidates above the threshold or at it with tie rank < r.  The
+// The tile's selection: keys above the window (the mask), and the candidates
+// above the threshold or at it with tie rank < r.  The
 // candidates are in ascending position order, so a key at the threshold ranks
 // after tile_eq_before[tile] of them in earlier tiles and after those at the
 // threshold before it in the list.  Lane c of each wavefront then holds word c
@@ -581,11 +621,14 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   const dim3 block(kBlock), tiles(g.num_tiles), tensors(g.T);
   hipLaunchKernelGGL(topk_reset, dim3(stride_grid(static_cast<int64_t>(g.T) * kMaxBins)), block, 0,
                      s, g, a);
-  hipLaunchKernelGGL(topk_hist0<G>, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL(topk_pass1<G>, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift0);
-  hipLaunchKernelGGL(topk_hist1, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL(topk_check, dim3(static_cast<unsigned>((g.T + kBlock - 1) / kBlock)), block, 0, s,
+                     g, a);
+  hipLaunchKernelGGL(topk_refill<G>, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL((topk_hist_cand<kShift1, 11>), tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift1);
-  hipLaunchKernelGGL(topk_hist2, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL((topk_hist_cand<kShift2, 9>), tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<9>, tensors, block, 0, s, a, kShift2);
   hipLaunchKernelGGL(topk_tile_counts, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);

@@ -106,6 +106,19 @@ def test_cltk_all_keys_equal():
     _run(wl, 0.3, wl.steps, grads_fn=grads_fn, memory=memory)
 
 
+def test_cltk_threshold_jumps():
+    """The select prepares its candidates for a window around the previous
+    exchange's threshold: gradient scales that swing by 1000x between
+    exchanges move the threshold far outside it (the fallback path), steady
+    ones keep it inside (the predicted path); both must give the same results."""
+    wl = _wl("cltk_jumps_w3", RAGGED, 3, steps=8)
+    scales = (1.0, 1.0, 1e3, 1e3, 1.0, 1e-3, 1e-3, 1.0)
+
+    def grads_fn(k):
+        return grads_for_step(wl, k, "cuda") * scales[k]
+    _run(wl, 0.05, wl.steps, grads_fn=grads_fn)
+
+
 def test_cltk_configure_rejects_bad_density():
     from error_compensated_bit_02_amd import OneBitAdam, OneBitError
     ctx = OneBitAdam((100, 7), 2, "f32", 0.9, 1e-8)
