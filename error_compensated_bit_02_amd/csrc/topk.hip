@@ -262,29 +262,50 @@ __global__ __launch_bounds__(kBlock) void topk_refill(Geometry g, TopkArgs a) {
   }
 }
 
-// Digits 1 and 2 over the candidates only: the histogram of
+// Digits 1 and 2 over the candidates only: per-tensor histograms of
 // (key >> kShiftD) & (2^kBits - 1) over the candidates whose higher bits equal
-// the prefix found so far.  A tile without candidates returns at once.
+// the prefix found so far.  A tile holds few candidates, so a workgroup walks
+// kCandTiles consecutive tiles with one LDS histogram, added to the tensor's
+// when the tensor changes and at the end.
+constexpr int kCandTiles = 16;
+
+template <int kBins>
+__device__ __forceinline__ void flush_bins(uint32_t *h, uint32_t *out) {
+  __syncthreads();   // every count of the tensor is in
+  for (int i = threadIdx.x; i < kBins; i += kBlock) {
+    if (h[i]) atomicAdd(&out[i], h[i]);
+    h[i] = 0u;
+  }
+  __syncthreads();   // zeroed before the next tensor's counts
+}
+
 template <int kShiftD, int kBits>
 __global__ __launch_bounds__(kBlock) void topk_hist_cand(Geometry g, TopkArgs a) {
   constexpr int kBins = 1 << kBits;
   constexpr int kHigh = kShiftD + kBits;   // bits above this digit are fixed
   __shared__ uint32_t h[kBins];
-  const uint32_t m = a.tile_m[blockIdx.x];
-  if (m == 0) return;   // uniform over the workgroup
-  const Tile tl = g.tiles[blockIdx.x];
-  const uint32_t want = a.prefix[tl.tensor] >> kHigh;
   for (int i = threadIdx.x; i < kBins; i += kBlock) h[i] = 0u;
   __syncthreads();
-  const uint32_t *cand = a.cand + tl.start;
-  for (uint32_t j = threadIdx.x; j < m; j += kBlock) {
-    const uint32_t key = cand[j];
-    if ((key >> kHigh) == want) atomicAdd(&h[(key >> kShiftD) & (kBins - 1)], 1u);
+  const int t0 = static_cast<int>(blockIdx.x) * kCandTiles;
+  const int t1 = min(t0 + kCandTiles, g.num_tiles);
+  int cur = -1;          // tensor whose counts h holds (uniform over the workgroup)
+  uint32_t want = 0u;
+  for (int tile = t0; tile < t1; ++tile) {
+    const uint32_t m = a.tile_m[tile];
+    if (m == 0) continue;   // uniform over the workgroup
+    const Tile tl = g.tiles[tile];
+    if (tl.tensor != cur) {
+      if (cur >= 0) flush_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins);
+      cur = tl.tensor;
+      want = a.prefix[cur] >> kHigh;
+    }
+    const uint32_t *cand = a.cand + tl.start;
+    for (uint32_t j = threadIdx.x; j < m; j += kBlock) {
+      const uint32_t key = cand[j];
+      if ((key >> kHigh) == want) atomicAdd(&h[(key >> kShiftD) & (kBins - 1)], 1u);
+    }
   }
-  __syncthreads();
-  uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
-  for (int i = threadIdx.x; i < kBins; i += kBlock)
-    if (h[i]) atomicAdd(&out[i], h[i]);
+  if (cur >= 0) flush_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins);
 }
 
 // One workgroup per tensor: the digit bin holding the krem-th largest key.
@@ -626,9 +647,10 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(topk_check, dim3(static_cast<unsigned>((g.T + kBlock - 1) / kBlock)), block, 0, s,
                      g, a);
   hipLaunchKernelGGL(topk_refill<G>, tiles, block, 0, s, g, a);
-  hipLaunchKernelGGL((topk_hist_cand<kShift1, 11>), tiles, block, 0, s, g, a);
+  const dim3 cand_grid(static_cast<unsigned>((g.num_tiles + kCandTiles - 1) / kCandTiles));
+  hipLaunchKernelGGL((topk_hist_cand<kShift1, 11>), cand_grid, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift1);
-  hipLaunchKernelGGL((topk_hist_cand<kShift2, 9>), tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL((topk_hist_cand<kShift2, 9>), cand_grid, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_pick<9>, tensors, block, 0, s, a, kShift2);
   hipLaunchKernelGGL(topk_tile_counts, tiles, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);
