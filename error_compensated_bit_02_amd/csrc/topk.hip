@@ -150,9 +150,9 @@ __device__ __forceinline__ void leader_keys(const Geometry &g, const TopkArgs &a
 // positions, compacted in ascending position order (cand, cand_pos, tile_m).
 // Workgroup-uniform call; wcnt holds 2 * kWaves counters.
 template <bool kFull>
-__device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, const TileLanes &ln,
-                                            const uint32_t (&key)[kPerLane], Window w,
-                                            uint32_t *wcnt) {
+__device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, int tile,
+                                            const TileLanes &ln, const uint32_t (&key)[kPerLane],
+                                            Window w, uint32_t *wcnt) {
   uint32_t nm = 0, ngt = 0;
   uint64_t gtw = 0;   // lane c: word c of the above-window mask
 #pragma unroll
@@ -194,9 +194,9 @@ __device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, c
       m += wcnt[v];
       gt += wcnt[kWaves + v];
     }
-    a.tile_m[blockIdx.x] = m;
-    a.tile_gt[blockIdx.x] = gt;   // completed by topk_tile_counts
-    a.tile_eq[blockIdx.x] = 0u;
+    a.tile_m[tile] = m;
+    a.tile_gt[tile] = gt;   // completed by topk_tile_counts
+    a.tile_eq[tile] = 0u;
   }
 }
 
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kBlock) void topk_pass1(Geometry g, TopkArgs a) {
   __shared__ uint32_t wcnt[2 * kWaves];
   for (int i = threadIdx.x; i < kMaxBins; i += kBlock) h[i] = 0u;
   __syncthreads();
-  const Tile tl = g.tiles[blockIdx.x];
+  const int tile = static_cast<int>(blockIdx.x);
+  const Tile tl = g.tiles[tile];
   const TileLanes ln = tile_lanes(tl);
   const Window w = predicted_window(a, tl.tensor);
   uint32_t key[kPerLane];
@@ -221,9 +222,9 @@ __global__ __launch_bounds__(kBlock) void topk_pass1(Geometry g, TopkArgs a) {
     if (ln.sub0 + 64 * c + ln.lane < tl.len) atomicAdd(&h[key[c] >> kShift0], 1u);
   if (w.lo <= w.hi) {   // uniform over the workgroup
     if (tl.len == kTile)
-      window_tile<true>(a, tl, ln, key, w, wcnt);
+      window_tile<true>(a, tl, tile, ln, key, w, wcnt);
     else
-      window_tile<false>(a, tl, ln, key, w, wcnt);
+      window_tile<false>(a, tl, tile, ln, key, w, wcnt);
   }
   __syncthreads();
   uint32_t *out = a.hist + static_cast<size_t>(tl.tensor) * kMaxBins;
@@ -231,86 +232,155 @@ __global__ __launch_bounds__(kBlock) void topk_pass1(Geometry g, TopkArgs a) {
     if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
-// After digit 0 is known: whether it fell in the predicted window (if not,
-// the fallback pass rebuilds the tensor's per-tile data), and the prediction
-// for the next exchange.
-__global__ __launch_bounds__(kBlock) void topk_check(Geometry g, TopkArgs a) {
-  const int t = blockIdx.x * kBlock + threadIdx.x;
-  if (t >= g.T) return;
-  const Window w = predicted_window(a, t);
-  const uint32_t b0 = a.prefix[t] >> kShift0;
-  a.miss[t] = (w.lo <= w.hi && b0 >= w.lo && b0 <= w.hi) ? 0u : 1u;
-  a.pred[t] = b0;
-}
+// Fallback: for the tensors whose digit 0 missed the window (topk_pick at
+// digit 0 sets a.miss), the per-tile data for the window [b0, b0], from the
+// leader's memory and gradient again.  A workgroup checks kRefillTiles tiles
+// at once and refills those of a missed tensor, so that an exchange without a
+// miss costs only the check.
+constexpr int kRefillTiles = 16;
 
-// Fallback: for the tensors whose digit 0 missed the window, the per-tile
-// data for the window [b0, b0], from the leader's memory and gradient again.
 template <typename G>
 __global__ __launch_bounds__(kBlock) void topk_refill(Geometry g, TopkArgs a) {
   __shared__ uint32_t wcnt[2 * kWaves];
-  const Tile tl = g.tiles[blockIdx.x];
-  if (a.miss[tl.tensor] == 0u) return;   // uniform over the workgroup
-  const TileLanes ln = tile_lanes(tl);
-  const uint32_t b0 = a.prefix[tl.tensor] >> kShift0;
-  uint32_t key[kPerLane];
-  if (tl.len == kTile) {
-    leader_keys<G, true>(g, a, tl, ln, key);
-    window_tile<true>(a, tl, ln, key, Window{b0, b0}, wcnt);
-  } else {
-    leader_keys<G, false>(g, a, tl, ln, key);
-    window_tile<false>(a, tl, ln, key, Window{b0, b0}, wcnt);
+  __shared__ uint32_t todo_s;
+  const int t0 = static_cast<int>(blockIdx.x) * kRefillTiles;
+  if (threadIdx.x < 64) {   // wavefront 0: which of the tiles belong to a missed tensor
+    const int tile = t0 + static_cast<int>(threadIdx.x);
+    const bool need = threadIdx.x < kRefillTiles && tile < g.num_tiles &&
+                      a.miss[g.tiles[tile].tensor] != 0u;
+    const uint64_t b = __ballot(need);
+    if (threadIdx.x == 0) todo_s = static_cast<uint32_t>(b);
+  }
+  __syncthreads();
+  for (uint32_t todo = __builtin_amdgcn_readfirstlane(todo_s); todo != 0u; todo &= todo - 1u) {
+    const int tile = t0 + __builtin_ctz(todo);   // uniform over the workgroup
+    const Tile tl = g.tiles[tile];
+    const TileLanes ln = tile_lanes(tl);
+    const uint32_t b0 = a.prefix[tl.tensor] >> kShift0;
+    uint32_t key[kPerLane];
+    if (tl.len == kTile) {
+      leader_keys<G, true>(g, a, tl, ln, key);
+      window_tile<true>(a, tl, tile, ln, key, Window{b0, b0}, wcnt);
+    } else {
+      leader_keys<G, false>(g, a, tl, ln, key);
+      window_tile<false>(a, tl, tile, ln, key, Window{b0, b0}, wcnt);
+    }
+    __syncthreads();   // wcnt is read before the next tile writes it
   }
 }
 
-// Digits 1 and 2 over the candidates only: per-tensor histograms of
-// (key >> kShiftD) & (2^kBits - 1) over the candidates whose higher bits equal
-// the prefix found so far.  A tile holds few candidates, so a workgroup walks
-// kCandTiles consecutive tiles with one LDS histogram, added to the tensor's
-// when the tensor changes and at the end.
-constexpr int kCandTiles = 16;
+// ---------------------------------------------------------------------------
+// kernels over the candidates only.  A tile holds a few hundred candidates,
+// so each wavefront takes kWaveTiles consecutive tiles on its own (no
+// workgroup barrier), keeps their counts, tensors and starts in its first
+// lanes, and keeps kCandUnroll candidate loads in flight per lane.
+// ---------------------------------------------------------------------------
+constexpr int kCandTiles = 16;                     // tiles per workgroup
+constexpr int kWaveTiles = kCandTiles / kWaves;    // tiles per wavefront
+constexpr int kCandUnroll = 4;
+static_assert(kWaveTiles * kWaves == kCandTiles && kWaveTiles <= 64, "tiles per wavefront");
 
+// Orders one wavefront's LDS accesses across its lanes: the hardware runs a
+// wavefront's LDS instructions in issue order; the fences keep the compiler
+// from moving accesses across this point.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct WaveTile {
+  uint32_t m;       // candidates in the tile (0 past the last tile)
+  int32_t tensor;
+  int64_t start;
+};
+
+// Lane j < kWaveTiles: the wavefront's tile tw0 + j.
+__device__ __forceinline__ WaveTile wave_tiles(const Geometry &g, const TopkArgs &a, int tw0, int lane) {
+  WaveTile r{0u, 0, 0};
+  const int tile = tw0 + lane;
+  if (lane < kWaveTiles && tile < g.num_tiles) {
+    r.m = a.tile_m[tile];
+    const Tile tl = g.tiles[tile];
+    r.tensor = tl.tensor;
+    r.start = tl.start;
+  }
+  return r;
+}
+
+// Tile j of the wavefront, as wave-uniform values.
+__device__ __forceinline__ WaveTile wave_tile_at(const WaveTile &w, int j) {
+  WaveTile r;
+  r.m = __builtin_amdgcn_readlane(w.m, j);
+  r.tensor = __builtin_amdgcn_readlane(w.tensor, j);
+  r.start = static_cast<int64_t>(readlane64(static_cast<uint64_t>(w.start), j));
+  return r;
+}
+
+// Adds the wavefront's histogram h into out and clears it.
 template <int kBins>
-__device__ __forceinline__ void flush_bins(uint32_t *h, uint32_t *out) {
-  __syncthreads();   // every count of the tensor is in
-  for (int i = threadIdx.x; i < kBins; i += kBlock) {
-    if (h[i]) atomicAdd(&out[i], h[i]);
-    h[i] = 0u;
+__device__ __forceinline__ void flush_wave_bins(uint32_t *h, uint32_t *out, int lane) {
+  wave_sync();   // every count of the tensor is in
+  for (int i = lane; i < kBins; i += 64) {
+    const uint32_t v = h[i];
+    if (v) {
+      atomicAdd(&out[i], v);
+      h[i] = 0u;
+    }
   }
-  __syncthreads();   // zeroed before the next tensor's counts
+  wave_sync();   // cleared before the next tensor's counts
 }
 
+// Digits 1 and 2: per-tensor histograms of (key >> kShiftD) & (2^kBits - 1)
+// over the candidates whose higher bits equal the prefix found so far, one
+// LDS histogram per wavefront, added to the tensor's when the wavefront's
+// tensor changes and at the end.
 template <int kShiftD, int kBits>
 __global__ __launch_bounds__(kBlock) void topk_hist_cand(Geometry g, TopkArgs a) {
   constexpr int kBins = 1 << kBits;
   constexpr int kHigh = kShiftD + kBits;   // bits above this digit are fixed
-  __shared__ uint32_t h[kBins];
-  for (int i = threadIdx.x; i < kBins; i += kBlock) h[i] = 0u;
-  __syncthreads();
-  const int t0 = static_cast<int>(blockIdx.x) * kCandTiles;
-  const int t1 = min(t0 + kCandTiles, g.num_tiles);
-  int cur = -1;          // tensor whose counts h holds (uniform over the workgroup)
+  __shared__ uint32_t hs[kWaves][kBins];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t *h = hs[wave];
+  for (int i = lane; i < kBins; i += 64) h[i] = 0u;
+  wave_sync();
+  const int tw0 = static_cast<int>(blockIdx.x) * kCandTiles + wave * kWaveTiles;
+  const WaveTile mine = wave_tiles(g, a, tw0, lane);
+  int cur = -1;   // tensor whose counts h holds (uniform over the wavefront)
   uint32_t want = 0u;
-  for (int tile = t0; tile < t1; ++tile) {
-    const uint32_t m = a.tile_m[tile];
-    if (m == 0) continue;   // uniform over the workgroup
-    const Tile tl = g.tiles[tile];
-    if (tl.tensor != cur) {
-      if (cur >= 0) flush_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins);
-      cur = tl.tensor;
+  for (int j = 0; j < kWaveTiles; ++j) {
+    const WaveTile wt = wave_tile_at(mine, j);
+    if (wt.m == 0u) continue;
+    if (wt.tensor != cur) {
+      if (cur >= 0) flush_wave_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins, lane);
+      cur = wt.tensor;
       want = a.prefix[cur] >> kHigh;
     }
-    const uint32_t *cand = a.cand + tl.start;
-    for (uint32_t j = threadIdx.x; j < m; j += kBlock) {
-      const uint32_t key = cand[j];
-      if ((key >> kHigh) == want) atomicAdd(&h[(key >> kShiftD) & (kBins - 1)], 1u);
+    const uint32_t *cand = a.cand + wt.start;
+    for (uint32_t j0 = 0; j0 < wt.m; j0 += 64 * kCandUnroll) {
+      uint32_t key[kCandUnroll];
+#pragma unroll
+      for (int u = 0; u < kCandUnroll; ++u) {   // all loads first
+        const uint32_t i = j0 + 64 * u + lane;
+        key[u] = i < wt.m ? cand[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kCandUnroll; ++u) {
+        const uint32_t i = j0 + 64 * u + lane;
+        if (i < wt.m && (key[u] >> kHigh) == want) atomicAdd(&h[(key[u] >> kShiftD) & (kBins - 1)], 1u);
+      }
     }
   }
-  if (cur >= 0) flush_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins);
+  if (cur >= 0) flush_wave_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins, lane);
 }
 
 // One workgroup per tensor: the digit bin holding the krem-th largest key.
-// Thread b owns bins kPer b .. kPer b + kPer - 1.
-template <int kBits>
+// Thread b owns bins kPer b .. kPer b + kPer - 1.  At digit 0 (kFirst) it
+// also records whether the bin lies in the window pass 1 prepared (if not,
+// the fallback pass rebuilds the tensor's per-tile data) and makes the bin
+// the next exchange's prediction.
+template <int kBits, bool kFirst>
 __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
   constexpr int kBins = 1 << kBits, kPer = kBins / kBlock;
   static_assert(kPer >= 1 && kBins <= kMaxBins, "digit width");
@@ -329,6 +399,7 @@ __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
   if (b == 0) {
     suf[kBlock] = 0u;
     krem_s = a.krem[t];   // read once, before the one writer below updates it
+    if (kFirst) a.miss[t] = 1u;   // overwritten below when the bin is found
   }
   __syncthreads();
   // suffix sums over threads: suf[b] = keys in the bins of threads >= b (Hillis-Steele)
@@ -343,8 +414,14 @@ __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
   if (above < krem && suf[b] >= krem) {   // exactly one thread holds the krem-th largest
     for (int j = kPer - 1; j >= 0; --j) {
       if (above + cnt[j] >= krem) {
-        a.prefix[t] |= static_cast<uint32_t>(b * kPer + j) << shift;
+        const uint32_t bin = static_cast<uint32_t>(b * kPer + j);
+        a.prefix[t] |= bin << shift;
         a.krem[t] = krem - above;
+        if (kFirst) {
+          const Window w = predicted_window(a, t);
+          a.miss[t] = (w.lo <= w.hi && bin >= w.lo && bin <= w.hi) ? 0u : 1u;
+          a.pred[t] = bin;
+        }
         break;
       }
       above += cnt[j];
@@ -358,74 +435,105 @@ __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
 // per-tile counts above and at the threshold, then per-tensor offsets
 // ---------------------------------------------------------------------------
 // Keys above the window were counted with the candidates; the candidates
-// give the rest.  A tile without candidates returns at once.
+// give the rest.  Wavefronts take their tiles as in topk_hist_cand.
 __global__ __launch_bounds__(kBlock) void topk_tile_counts(Geometry g, TopkArgs a) {
-  __shared__ uint32_t cnt[2][kWaves];
-  const uint32_t m = a.tile_m[blockIdx.x];
-  if (m == 0) return;   // uniform over the workgroup
-  const Tile tl = g.tiles[blockIdx.x];
-  const uint32_t tau = a.prefix[tl.tensor];
-  const uint32_t *cand = a.cand + tl.start;
-  uint32_t gt = 0, eq = 0;
-  for (uint32_t j0 = 0; j0 < m; j0 += kBlock) {   // uniform trip count: ballots stay converged
-    const uint32_t j = j0 + threadIdx.x;
-    const uint32_t key = j < m ? cand[j] : 0u;
-    gt += __popcll(__ballot(j < m && key > tau));
-    eq += __popcll(__ballot(j < m && key == tau));
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    cnt[0][wave] = gt;
-    cnt[1][wave] = eq;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t sg = 0, se = 0;
-    for (int v = 0; v < kWaves; ++v) {
-      sg += cnt[0][v];
-      se += cnt[1][v];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tw0 = static_cast<int>(blockIdx.x) * kCandTiles + wave * kWaveTiles;
+  const WaveTile mine = wave_tiles(g, a, tw0, lane);
+  const uint32_t tau_l = mine.m != 0u ? a.prefix[mine.tensor] : 0u;
+  for (int j = 0; j < kWaveTiles; ++j) {
+    const WaveTile wt = wave_tile_at(mine, j);
+    if (wt.m == 0u) continue;
+    const uint32_t tau = __builtin_amdgcn_readlane(tau_l, j);
+    const uint32_t *cand = a.cand + wt.start;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t j0 = 0; j0 < wt.m; j0 += 64 * kCandUnroll) {   // uniform: ballots stay converged
+      uint32_t key[kCandUnroll];
+#pragma unroll
+      for (int u = 0; u < kCandUnroll; ++u) {
+        const uint32_t i = j0 + 64 * u + lane;
+        key[u] = i < wt.m ? cand[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kCandUnroll; ++u) {
+        const bool valid = j0 + 64 * u + lane < wt.m;
+        gt += __popcll(__ballot(valid && key[u] > tau));
+        eq += __popcll(__ballot(valid && key[u] == tau));
+      }
     }
-    a.tile_gt[blockIdx.x] += sg;
-    a.tile_eq[blockIdx.x] = se;
+    if (lane == 0) {
+      a.tile_gt[tw0 + j] += gt;
+      a.tile_eq[tw0 + j] = eq;
+    }
   }
 }
 
+// Exclusive scan of v over the workgroup's threads; total gets the sum.
+__device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t *s, int64_t &total) {
+  s[threadIdx.x] = v;
+  __syncthreads();
+  for (int d = 1; d < kBlock; d <<= 1) {   // inclusive (Hillis-Steele)
+    const int64_t add = threadIdx.x >= static_cast<unsigned>(d) ? s[threadIdx.x - d] : 0;
+    __syncthreads();
+    s[threadIdx.x] += add;
+    __syncthreads();
+  }
+  total = s[kBlock - 1];
+  const int64_t incl = s[threadIdx.x];
+  __syncthreads();   // s may be written again
+  return incl - v;
+}
+
+// Tiles of topk_offsets per thread and round: a thread scans its run of
+// consecutive tiles itself, the workgroup scans the runs' totals.
+constexpr int kRun = 16;
+
+// The number of keys at the threshold in a tile that are taken, given those
+// at the threshold in earlier tiles (ties go to the lowest positions).
+__device__ __forceinline__ int64_t taken_ties(int64_t r, int64_t eq_before, int64_t eq) {
+  return eq_before >= r ? 0 : (r - eq_before < eq ? r - eq_before : eq);
+}
+
 // One workgroup per tensor: exclusive scans over the tensor's tiles of the
-// keys at the threshold and of the selected entries (ties taken in order).
+// keys at the threshold and of the selected entries.
 __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
-  __shared__ int64_t sa[kBlock], sb[kBlock];
+  __shared__ int64_t s[kBlock];
   const int t = blockIdx.x;
   const int first = g.tile_begin[t], last = g.tile_begin[t + 1];
   const int64_t r = a.krem[t];   // keys equal to the threshold that are taken
   int64_t eq_base = 0, sel_base = a.k_off[t];
-  for (int c0 = first; c0 < last; c0 += kBlock) {
-    const int i = c0 + threadIdx.x;
-    const int64_t eq = i < last ? a.tile_eq[i] : 0;
-    sa[threadIdx.x] = eq;
-    __syncthreads();
-    for (int d = 1; d < kBlock; d <<= 1) {   // inclusive scan of eq
-      const int64_t add = threadIdx.x >= d ? sa[threadIdx.x - d] : 0;
-      __syncthreads();
-      sa[threadIdx.x] += add;
-      __syncthreads();
+  for (int c0 = first; c0 < last; c0 += kBlock * kRun) {   // uniform over the workgroup
+    const int i0 = c0 + static_cast<int>(threadIdx.x) * kRun;
+    uint32_t eq[kRun], gt[kRun];
+    int64_t my_eq = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const bool ok = i0 + j < last;
+      eq[j] = ok ? a.tile_eq[i0 + j] : 0u;
+      gt[j] = ok ? a.tile_gt[i0 + j] : 0u;
+      my_eq += eq[j];
     }
-    const int64_t eq_before = eq_base + sa[threadIdx.x] - eq;
-    const int64_t take = eq_before >= r ? 0 : (r - eq_before < eq ? r - eq_before : eq);
-    const int64_t sel = i < last ? a.tile_gt[i] + take : 0;
-    sb[threadIdx.x] = sel;
-    __syncthreads();
-    for (int d = 1; d < kBlock; d <<= 1) {   // inclusive scan of sel
-      const int64_t add = threadIdx.x >= d ? sb[threadIdx.x - d] : 0;
-      __syncthreads();
-      sb[threadIdx.x] += add;
-      __syncthreads();
+    int64_t eq_tot, sel_tot;
+    const int64_t eq0 = eq_base + block_exclusive_scan(my_eq, s, eq_tot);
+    int64_t run = eq0, my_sel = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      my_sel += gt[j] + taken_ties(r, run, eq[j]);
+      run += eq[j];
     }
-    if (i < last) {
-      a.tile_eq_before[i] = eq_before;
-      a.tile_sel_off[i] = sel_base + sb[threadIdx.x] - sel;
+    const int64_t sel0 = sel_base + block_exclusive_scan(my_sel, s, sel_tot);
+    run = eq0;
+    int64_t at = sel0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      if (i0 + j < last) {
+        a.tile_eq_before[i0 + j] = run;
+        a.tile_sel_off[i0 + j] = at;
+      }
+      at += gt[j] + taken_ties(r, run, eq[j]);
+      run += eq[j];
     }
-    const int64_t eq_tot = sa[kBlock - 1], sel_tot = sb[kBlock - 1];
-    __syncthreads();
     eq_base += eq_tot;
     sel_base += sel_tot;
   }
@@ -643,16 +751,15 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(topk_reset, dim3(stride_grid(static_cast<int64_t>(g.T) * kMaxBins)), block, 0,
                      s, g, a);
   hipLaunchKernelGGL(topk_pass1<G>, tiles, block, 0, s, g, a);
-  hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift0);
-  hipLaunchKernelGGL(topk_check, dim3(static_cast<unsigned>((g.T + kBlock - 1) / kBlock)), block, 0, s,
-                     g, a);
-  hipLaunchKernelGGL(topk_refill<G>, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL((topk_pick<11, true>), tensors, block, 0, s, a, kShift0);
+  hipLaunchKernelGGL(topk_refill<G>, dim3(static_cast<unsigned>((g.num_tiles + kRefillTiles - 1) / kRefillTiles)),
+                     block, 0, s, g, a);
   const dim3 cand_grid(static_cast<unsigned>((g.num_tiles + kCandTiles - 1) / kCandTiles));
   hipLaunchKernelGGL((topk_hist_cand<kShift1, 11>), cand_grid, block, 0, s, g, a);
-  hipLaunchKernelGGL(topk_pick<11>, tensors, block, 0, s, a, kShift1);
+  hipLaunchKernelGGL((topk_pick<11, false>), tensors, block, 0, s, a, kShift1);
   hipLaunchKernelGGL((topk_hist_cand<kShift2, 9>), cand_grid, block, 0, s, g, a);
-  hipLaunchKernelGGL(topk_pick<9>, tensors, block, 0, s, a, kShift2);
-  hipLaunchKernelGGL(topk_tile_counts, tiles, block, 0, s, g, a);
+  hipLaunchKernelGGL((topk_pick<9, false>), tensors, block, 0, s, a, kShift2);
+  hipLaunchKernelGGL(topk_tile_counts, cand_grid, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);
 }
 
