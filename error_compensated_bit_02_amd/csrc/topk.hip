@@ -100,7 +100,7 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
 constexpr int kMaxBins = 2048;
 constexpr int kShift0 = 20, kShift1 = 9, kShift2 = 0;
 constexpr uint32_t kNoBin = 0xffffffffu;     // no prediction yet
-constexpr uint32_t kWindowBelow = 2, kWindowAbove = 4;   // the threshold's bin drifts upward
+constexpr uint32_t kWindowBelow = 1, kWindowAbove = 3;   // the threshold's bin drifts upward
 
 // Grid-stride launches (grid capped at kStrideBlocks) for the two kernels
 // whose size is not a tile count.
@@ -148,7 +148,8 @@ __device__ __forceinline__ void leader_keys(const Geometry &g, const TopkArgs &a
 // Per tile, for the digit-0 window [w.lo, w.hi]: the bit mask of keys above
 // it (a.above), their count (tile_gt), and the keys inside it with their
 // positions, compacted in ascending position order (cand, cand_pos, tile_m).
-// Workgroup-uniform call; wcnt holds 2 * kWaves counters.
+// Workgroup-uniform call; wcnt holds 2 * kWaves counters (a caller that
+// writes them again must pass a barrier first).
 template <bool kFull>
 __device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, int tile,
                                             const TileLanes &ln, const uint32_t (&key)[kPerLane],
@@ -170,6 +171,16 @@ __device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, i
     wcnt[kWaves + ln.wave] = ngt;
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0, gt = 0;
+    for (int v = 0; v < kWaves; ++v) {
+      m += wcnt[v];
+      gt += wcnt[kWaves + v];
+    }
+    a.tile_m[tile] = m;
+    a.tile_gt[tile] = gt;   // completed by topk_tile_counts
+    a.tile_eq[tile] = 0u;
+  }
   uint32_t at = 0;   // this wavefront's first slot in the tile's candidate list
   for (int v = 0; v < ln.wave; ++v) at += wcnt[v];
   uint32_t *cand = a.cand + tl.start;
@@ -186,17 +197,6 @@ __device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, i
       cand_pos[slot] = static_cast<uint16_t>(ln.sub0 + 64 * c + ln.lane);
     }
     at += __popcll(bm);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = 0, gt = 0;
-    for (int v = 0; v < kWaves; ++v) {
-      m += wcnt[v];
-      gt += wcnt[kWaves + v];
-    }
-    a.tile_m[tile] = m;
-    a.tile_gt[tile] = gt;   // completed by topk_tile_counts
-    a.tile_eq[tile] = 0u;
   }
 }
 
@@ -295,11 +295,12 @@ struct WaveTile {
   int64_t start;
 };
 
-// Lane j < kWaveTiles: the wavefront's tile tw0 + j.
+// Lane j < kN: the wavefront's tile tw0 + j.
+template <int kN>
 __device__ __forceinline__ WaveTile wave_tiles(const Geometry &g, const TopkArgs &a, int tw0, int lane) {
   WaveTile r{0u, 0, 0};
   const int tile = tw0 + lane;
-  if (lane < kWaveTiles && tile < g.num_tiles) {
+  if (lane < kN && tile < g.num_tiles) {
     r.m = a.tile_m[tile];
     const Tile tl = g.tiles[tile];
     r.tensor = tl.tensor;
@@ -331,10 +332,10 @@ __device__ __forceinline__ void flush_wave_bins(uint32_t *h, uint32_t *out, int 
   wave_sync();   // cleared before the next tensor's counts
 }
 
-// Digits 1 and 2: per-tensor histograms of (key >> kShiftD) & (2^kBits - 1)
-// over the candidates whose higher bits equal the prefix found so far, one
-// LDS histogram per wavefront, added to the tensor's when the wavefront's
-// tensor changes and at the end.
+// Per-tensor histograms of (key >> kShiftD) & (2^kBits - 1) over the
+// candidates whose higher bits equal the prefix found so far, one LDS
+// histogram per wavefront, added to the tensor's when the wavefront's tensor
+// changes and at the end.  Used for digit 2, which few candidates reach.
 template <int kShiftD, int kBits>
 __global__ __launch_bounds__(kBlock) void topk_hist_cand(Geometry g, TopkArgs a) {
   constexpr int kBins = 1 << kBits;
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(kBlock) void topk_hist_cand(Geometry g, TopkArgs a)
   for (int i = lane; i < kBins; i += 64) h[i] = 0u;
   wave_sync();
   const int tw0 = static_cast<int>(blockIdx.x) * kCandTiles + wave * kWaveTiles;
-  const WaveTile mine = wave_tiles(g, a, tw0, lane);
+  const WaveTile mine = wave_tiles<kWaveTiles>(g, a, tw0, lane);
   int cur = -1;   // tensor whose counts h holds (uniform over the wavefront)
   uint32_t want = 0u;
   for (int j = 0; j < kWaveTiles; ++j) {
@@ -373,6 +374,62 @@ __global__ __launch_bounds__(kBlock) void topk_hist_cand(Geometry g, TopkArgs a)
     }
   }
   if (cur >= 0) flush_wave_bins<kBins>(h, a.hist + static_cast<size_t>(cur) * kMaxBins, lane);
+}
+
+// Digit 1: the candidates in the threshold's first-digit bin spread evenly
+// over the 2048 bins, so per-wavefront histograms would add nearly one
+// global atomic per candidate.  One LDS histogram per workgroup over
+// kSharedTiles tiles, for the tensor of its first tile, aggregates ~4x more;
+// candidates of other tensors go to their tensor's histogram directly.
+constexpr int kSharedTiles = 64;
+constexpr int kSharedWaveTiles = kSharedTiles / kWaves;
+constexpr int kSharedUnroll = 8;
+static_assert(kSharedWaveTiles * kWaves == kSharedTiles && kSharedWaveTiles <= 64, "tiles per wavefront");
+
+template <int kShiftD, int kBits>
+__global__ __launch_bounds__(kBlock) void topk_hist_shared(Geometry g, TopkArgs a) {
+  constexpr int kBins = 1 << kBits;
+  constexpr int kHigh = kShiftD + kBits;   // bits above this digit are fixed
+  __shared__ uint32_t h[kBins];
+  for (int i = threadIdx.x; i < kBins; i += kBlock) h[i] = 0u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = static_cast<int>(blockIdx.x) * kSharedTiles;
+  const int main_t = g.tiles[t0].tensor;   // the tensor h counts for
+  const uint32_t main_want = a.prefix[main_t] >> kHigh;
+  const WaveTile mine = wave_tiles<kSharedWaveTiles>(g, a, t0 + wave * kSharedWaveTiles, lane);
+  for (int j = 0; j < kSharedWaveTiles; ++j) {
+    const WaveTile wt = wave_tile_at(mine, j);
+    if (wt.m == 0u) continue;
+    const bool local = wt.tensor == main_t;   // uniform over the wavefront
+    const uint32_t want = local ? main_want : a.prefix[wt.tensor] >> kHigh;
+    uint32_t *gh = a.hist + static_cast<size_t>(wt.tensor) * kMaxBins;
+    const uint32_t *cand = a.cand + wt.start;
+    for (uint32_t j0 = 0; j0 < wt.m; j0 += 64 * kSharedUnroll) {
+      uint32_t key[kSharedUnroll];
+#pragma unroll
+      for (int u = 0; u < kSharedUnroll; ++u) {   // all loads first
+        const uint32_t i = j0 + 64 * u + lane;
+        key[u] = i < wt.m ? cand[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kSharedUnroll; ++u) {
+        const uint32_t i = j0 + 64 * u + lane;
+        if (i < wt.m && (key[u] >> kHigh) == want) {
+          const uint32_t bin = (key[u] >> kShiftD) & (kBins - 1);
+          if (local)
+            atomicAdd(&h[bin], 1u);
+          else
+            atomicAdd(&gh[bin], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t *out = a.hist + static_cast<size_t>(main_t) * kMaxBins;
+  for (int i = threadIdx.x; i < kBins; i += kBlock)
+    if (h[i]) atomicAdd(&out[i], h[i]);
 }
 
 // One workgroup per tensor: the digit bin holding the krem-th largest key.
@@ -440,7 +497,7 @@ __global__ __launch_bounds__(kBlock) void topk_tile_counts(Geometry g, TopkArgs 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tw0 = static_cast<int>(blockIdx.x) * kCandTiles + wave * kWaveTiles;
-  const WaveTile mine = wave_tiles(g, a, tw0, lane);
+  const WaveTile mine = wave_tiles<kWaveTiles>(g, a, tw0, lane);
   const uint32_t tau_l = mine.m != 0u ? a.prefix[mine.tensor] : 0u;
   for (int j = 0; j < kWaveTiles; ++j) {
     const WaveTile wt = wave_tile_at(mine, j);
@@ -755,7 +812,9 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(topk_refill<G>, dim3(static_cast<unsigned>((g.num_tiles + kRefillTiles - 1) / kRefillTiles)),
                      block, 0, s, g, a);
   const dim3 cand_grid(static_cast<unsigned>((g.num_tiles + kCandTiles - 1) / kCandTiles));
-  hipLaunchKernelGGL((topk_hist_cand<kShift1, 11>), cand_grid, block, 0, s, g, a);
+  hipLaunchKernelGGL((topk_hist_shared<kShift1, 11>),
+                     dim3(static_cast<unsigned>((g.num_tiles + kSharedTiles - 1) / kSharedTiles)), block, 0, s,
+                     g, a);
   hipLaunchKernelGGL((topk_pick<11, false>), tensors, block, 0, s, a, kShift1);
   hipLaunchKernelGGL((topk_hist_cand<kShift2, 9>), cand_grid, block, 0, s, g, a);
   hipLaunchKernelGGL((topk_pick<9, false>), tensors, block, 0, s, a, kShift2);
