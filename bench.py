@@ -105,7 +105,7 @@ def counter_traffic(workload: str, kernel: str):
 
 
 # rocprofv3 kernel names -> the library's kernel kinds.  Every topk_ kernel
-# but the gather and the average belongs to the CLT-k select stage (nine
+# but the gather and the average belongs to the CLT-k select stage (ten
 # launches); its bytes are summed per exchange (per topk_reset).
 
 
@@ -142,33 +142,43 @@ def summarize_counters(pmc_dir: str, workload: str) -> dict:
     from collections import defaultdict
 
     def load(tag):
+        """Mean counter bytes per launch of each kind, and the CLT-k select
+        stage's bytes of each exchange in dispatch order."""
         files = glob.glob(os.path.join(pmc_dir, tag, "**", "*counter_collection.csv"), recursive=True)
         if not files:
             raise SystemExit(f"no counter_collection.csv under {os.path.join(pmc_dir, tag)}")
-        total, resets = defaultdict(float), 0
-        launches = defaultdict(int)
+        rows = []
         for path in files:
             with open(path) as f:
-                for r in csv.DictReader(f):
-                    k = kind_of(r["Kernel_Name"])
-                    if k is None:
-                        continue
-                    total[k] += float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
-                    launches[k] += 1
-                    resets += "topk_reset" in r["Kernel_Name"]
-        if resets:
-            launches["cltk_select"] = resets   # one select stage per exchange
-        return {k: total[k] / launches[k] for k in total}
+                rows += [r for r in csv.DictReader(f)]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        total, launches, exchanges = defaultdict(float), defaultdict(int), []
+        for r in rows:
+            k = kind_of(r["Kernel_Name"])
+            if k is None:
+                continue
+            b = float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
+            total[k] += b
+            launches[k] += 1
+            if "topk_reset" in r["Kernel_Name"]:
+                exchanges.append(0.0)
+            if k == "cltk_select" and exchanges:
+                exchanges[-1] += b
+        if exchanges:
+            launches["cltk_select"] = len(exchanges)   # one select stage per exchange
+        return {k: total[k] / launches[k] for k in total}, exchanges
 
     copy_bytes = 1024 << 20
-    fetch_factor = copy_bytes / load("copy_FETCH_SIZE")["copy"]
-    write_factor = copy_bytes / load("copy_WRITE_SIZE")["copy"]
-    fetch, write = load("step_FETCH_SIZE"), load("step_WRITE_SIZE")
+    fetch_factor = copy_bytes / load("copy_FETCH_SIZE")[0]["copy"]
+    write_factor = copy_bytes / load("copy_WRITE_SIZE")[0]["copy"]
+    (fetch, fetch_x), (write, write_x) = load("step_FETCH_SIZE"), load("step_WRITE_SIZE")
     per = {k: round(fetch[k] * fetch_factor + write.get(k, 0.0) * write_factor)
            for k in fetch if k != "copy"}
+    per_exchange = [round(f * fetch_factor + w * write_factor) for f, w in zip(fetch_x, write_x)]
     return {"workload": workload, "sources_sha256": {s: sha256_of(s) for s in SOURCES},
             "fetch_factor": fetch_factor, "write_factor": write_factor,
             "copy_calibration_bytes": copy_bytes, "per_launch_bytes": per,
+            "cltk_select_bytes_per_exchange": per_exchange,
             "per_launch_fetch_bytes": {k: round(fetch[k] * fetch_factor) for k in per},
             "per_launch_write_bytes": {k: round(write.get(k, 0.0) * write_factor) for k in per}}
 
@@ -352,6 +362,29 @@ def copy_ceiling(gib: int = 4, reps: int = 5) -> dict:
             "median_ms": round(best, 4), "reps": reps, "frac": round(2 * 4 * n / (best * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def add_ceiling(gib: int = 4, reps: int = 5) -> dict:
+    """An in-place add e += g over two `gib` GiB arrays (two reads and one
+    write per element, the worker pass's mix), timed like copy_ceiling."""
+    import torch
+    n = gib << 28
+    g = torch.ones(n, device="cuda")
+    e = torch.zeros(n, device="cuda")
+    e.add_(g)
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e.add_(g)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del g, e
+    best = sorted(ms)[len(ms) // 2]
+    gbps = 3 * 4 * n / (best * 1e-3) / 1e9
+    return {"gbps": round(gbps, 1), "bytes_moved": 3 * 4 * n, "median_ms": round(best, 4), "reps": reps,
+            "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def step_counter_gbps(workload, per_kernel, ms_step, steps):
     """Whole-step HBM GB/s from the counter bytes of every kernel the step
     launched, or None when some kernel has no current counter figure."""
@@ -520,6 +553,10 @@ def main() -> int:
     result["cltk"] = cltk
     torch.cuda.empty_cache()
     result["copy_ceiling"] = copy_ceiling()
+    result["add_ceiling"] = add_ceiling()
+    log(f"bench: streaming ceilings: copy {result['copy_ceiling']['gbps']:.0f} GB/s, in-place add "
+        f"{result['add_ceiling']['gbps']:.0f} GB/s; {head['roofline']['kernel']} at "
+        f"{head['roofline']['achieved'] / result['add_ceiling']['gbps']:.1%} of the add")
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (cpu baseline)")
