@@ -419,24 +419,42 @@ __global__ __launch_bounds__(kBlock) void server_kernel(Geometry g, ServerArgs a
 // update from a server message: m = s_s*sign (stored if kStoreM),
 // p <- p - lr * (m / (sqrt(v) + eps))
 // ---------------------------------------------------------------------------
+// The update in chunks of kUpdChunk elements, one workgroup each (grid-stride
+// past the device's grid limit): lane l of wavefront v owns element
+// kUpdChunk/kWaves * v + 64*c + l of the chunk.  A single read-modify-write
+// stream streams faster in small workgroups taken in address order: on
+// MI355X an in-place add ran at ~5.9 TB/s with one workgroup per 4 KB piece
+// against ~5.3 TB/s with one per 32 KB.
+constexpr int kUpdChunk = 1024;
+constexpr int kUpdPerTile = kTile / kUpdChunk;
+constexpr int kUpdSub = kUpdChunk / kWaves;
+constexpr int kUpdPerLane = kUpdSub / 64;
+static_assert(kTile % kUpdChunk == 0 && kUpdSub % 64 == 0, "update chunk shape");
+
 template <bool kStoreM, bool kRatio, bool kFull>
-__device__ __forceinline__ void update_tile(const Tile &tl, const Geometry &g, const UpdateArgs &a) {
-  const Lanes ln = lanes_of<kFull>(tl);
-  const float ss = a.scale_s[g.tile_piece[blockIdx.x]];
+__device__ __forceinline__ void update_chunk(const Tile &tl, int tile, int q, const Geometry &g,
+                                             const UpdateArgs &a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub0 = q * kUpdChunk + wave * kUpdSub;   // first element of this wavefront in the tile
+  const int64_t base = tl.start + sub0;
+  const int rem = tl.len - sub0;
+  const int nwords = kFull ? kUpdPerLane : (rem <= 0 ? 0 : (rem >= kUpdSub ? kUpdPerLane : (rem + 63) / 64));
+  auto ok = [&](int c) { return kFull || sub0 + 64 * c + lane < tl.len; };
+  const float ss = a.scale_s[g.tile_piece[tile]];
   const float r = kRatio ? a.ratio[tl.tensor] : 1.0f;
-  const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
-  float vv[kPerLane], pv[kPerLane];
+  const uint64_t words = lane < nwords ? a.packed_s[(base >> 6) + lane] : 0ull;
+  float vv[kUpdPerLane], pv[kUpdPerLane];
 #pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
-    const bool ok = in_tile<kFull>(tl, ln, c);
-    vv[c] = ok ? a.v[ln.base + 64 * c + ln.lane] : 0.0f;
-    pv[c] = ok ? a.params[ln.base + 64 * c + ln.lane] : 0.0f;
+  for (int c = 0; c < kUpdPerLane; ++c) {
+    vv[c] = ok(c) ? a.v[base + 64 * c + lane] : 0.0f;
+    pv[c] = ok(c) ? a.params[base + 64 * c + lane] : 0.0f;
   }
 #pragma unroll
-  for (int c = 0; c < kPerLane; ++c) {
+  for (int c = 0; c < kUpdPerLane; ++c) {
     const float mv = signed_scale(words, c, ss);  // every lane takes part in the broadcast
-    if (!in_tile<kFull>(tl, ln, c)) continue;
-    const int64_t i = ln.base + 64 * c + ln.lane;
+    if (!ok(c)) continue;
+    const int64_t i = base + 64 * c + lane;
     const float d = __builtin_sqrtf(vv[c]) + a.eps;
     float u = mv / d;
     if (kStoreM) a.m[i] = mv;
@@ -451,11 +469,18 @@ __device__ __forceinline__ void update_tile(const Tile &tl, const Geometry &g, c
 
 template <bool kStoreM, bool kRatio>
 __global__ __launch_bounds__(kBlock) void update_kernel(Geometry g, UpdateArgs a) {
-  const Tile tl = g.tiles[blockIdx.x];
-  if (tl.len == kTile)
-    update_tile<kStoreM, kRatio, true>(tl, g, a);
-  else
-    update_tile<kStoreM, kRatio, false>(tl, g, a);
+  const int64_t chunks = static_cast<int64_t>(g.num_tiles) * kUpdPerTile;
+  for (int64_t b = blockIdx.x; b < chunks; b += gridDim.x) {   // uniform over the workgroup
+    const int tile = static_cast<int>(b / kUpdPerTile);
+    const int q = static_cast<int>(b % kUpdPerTile);
+    const Tile tl = g.tiles[tile];
+    const int rem = tl.len - q * kUpdChunk;
+    if (rem <= 0) continue;   // past the tile's end
+    if (rem >= kUpdChunk)
+      update_chunk<kStoreM, kRatio, true>(tl, tile, q, g, a);
+    else
+      update_chunk<kStoreM, kRatio, false>(tl, tile, q, g, a);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -692,7 +717,8 @@ void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipS
 
 void launch_update(bool store_m, bool with_ratio, const Geometry &g, const UpdateArgs &a,
                    hipStream_t s) {
-  const dim3 grid(g.num_tiles), block(kBlock);
+  const int64_t chunks = static_cast<int64_t>(g.num_tiles) * kUpdPerTile;
+  const dim3 grid(static_cast<unsigned>(chunks < kMaxGrid ? chunks : kMaxGrid)), block(kBlock);
   if (store_m && with_ratio)
     hipLaunchKernelGGL((update_kernel<true, true>), grid, block, 0, s, g, a);
   else if (store_m)
