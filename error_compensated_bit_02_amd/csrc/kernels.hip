@@ -590,48 +590,67 @@ __global__ __launch_bounds__(kBlock) void materialize_kernel(Geometry g, Materia
 //   gbar = (ascending sum over w of g_w) / W
 //   m = c1*m + c2*gbar;  v = b2*v + cb2*(gbar*gbar);  p -= lr * (m / (sqrt(v) + eps))
 // ---------------------------------------------------------------------------
+// The warmup step in the update's chunks (one workgroup per kUpdChunk
+// elements, grid-stride past the grid limit), the workers' gradients loaded
+// in groups of kGroup and added in ascending worker order.
 template <typename G, bool kFull, bool kPow2>
-__device__ __forceinline__ void warmup_tile(const Tile &tl, const Geometry &g, const WarmupArgs &a) {
-  const Lanes ln = lanes_of<kFull>(tl);
-  const G *grads = static_cast<const G *>(a.grads) + ln.base + ln.lane;
+__device__ __forceinline__ void warmup_chunk(const Tile &tl, int q, const Geometry &g, const WarmupArgs &a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub0 = q * kUpdChunk + wave * kUpdSub;
+  const int64_t base = tl.start + sub0;
+  auto ok = [&](int c) { return kFull || sub0 + 64 * c + lane < tl.len; };
+  const G *grads = static_cast<const G *>(a.grads) + base + lane;
   const float wf = static_cast<float>(g.W);
-  const float inv_w = 1.0f / wf;   // exact when W is a power of two
-  // eight elements per lane at a time keep the W-long sums in registers
-  constexpr int kChunk = 8;
+  const float inv_w = 1.0f / wf;
+  constexpr int kGroup = 8;
+  float acc[kUpdPerLane];
 #pragma unroll
-  for (int c0 = 0; c0 < kPerLane; c0 += kChunk) {
-    float acc[kChunk];
+  for (int j = 0; j < kUpdPerLane; ++j) acc[j] = 0.0f;
+  for (int w0 = 0; w0 < g.W; w0 += kGroup) {
+    float x[kGroup][kUpdPerLane];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) acc[j] = 0.0f;
-    for (int w = 0; w < g.W; ++w) {
-      const G *gw = grads + static_cast<size_t>(w) * g.N;
+    for (int k = 0; k < kGroup; ++k) {
+      const G *gw = grads + static_cast<size_t>(w0 + k) * g.N;
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j)
-        if (in_tile<kFull>(tl, ln, c0 + j)) acc[j] = acc[j] + grad_value(gw + 64 * (c0 + j));
+      for (int j = 0; j < kUpdPerLane; ++j) x[k][j] = (w0 + k < g.W && ok(j)) ? grad_value(gw + 64 * j) : 0.0f;
     }
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      if (!in_tile<kFull>(tl, ln, c0 + j)) continue;
-      const int64_t i = ln.base + 64 * (c0 + j) + ln.lane;
-      const float gbar = kPow2 ? acc[j] * inv_w : acc[j] / wf;
-      const float m = a.c1 * a.m[i] + a.c2 * gbar;
-      const float v = a.b2 * a.v[i] + a.cb2 * (gbar * gbar);
-      const float d = __builtin_sqrtf(v) + a.eps;
-      const float u = m / d;
-      a.m[i] = m;
-      a.v[i] = v;
-      a.params[i] = a.params[i] - a.lr * u;
+    for (int k = 0; k < kGroup; ++k) {
+      if (w0 + k >= g.W) break;
+#pragma unroll
+      for (int j = 0; j < kUpdPerLane; ++j) acc[j] = acc[j] + x[k][j];
     }
+  }
+#pragma unroll
+  for (int j = 0; j < kUpdPerLane; ++j) {
+    if (!ok(j)) continue;
+    const int64_t i = base + 64 * j + lane;
+    const float gbar = kPow2 ? acc[j] * inv_w : acc[j] / wf;
+    const float m = a.c1 * a.m[i] + a.c2 * gbar;
+    const float v = a.b2 * a.v[i] + a.cb2 * (gbar * gbar);
+    const float d = __builtin_sqrtf(v) + a.eps;
+    const float u = m / d;
+    a.m[i] = m;
+    a.v[i] = v;
+    a.params[i] = a.params[i] - a.lr * u;
   }
 }
 
 template <typename G, bool kPow2>
 __global__ __launch_bounds__(kBlock) void warmup_kernel(Geometry g, WarmupArgs a) {
-  const Tile tl = g.tiles[blockIdx.x];
-  if (tl.len == kTile)
-    warmup_tile<G, true, kPow2>(tl, g, a);
-  else
-    warmup_tile<G, false, kPow2>(tl, g, a);
+  const int64_t chunks = static_cast<int64_t>(g.num_tiles) * kUpdPerTile;
+  for (int64_t b = blockIdx.x; b < chunks; b += gridDim.x) {
+    const int tile = static_cast<int>(b / kUpdPerTile);
+    const int q = static_cast<int>(b % kUpdPerTile);
+    const Tile tl = g.tiles[tile];
+    const int rem = tl.len - q * kUpdChunk;
+    if (rem <= 0) continue;
+    if (rem >= kUpdChunk)
+      warmup_chunk<G, true, kPow2>(tl, q, g, a);
+    else
+      warmup_chunk<G, false, kPow2>(tl, q, g, a);
+  }
 }
 
 // Zero the worker and server errors (tensor ranges only; padding untouched).
@@ -743,7 +762,8 @@ void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t
 }
 
 void launch_warmup(const Geometry &g, bool bf16, const WarmupArgs &a, hipStream_t s) {
-  const dim3 grid(g.num_tiles), block(kBlock);
+  const int64_t chunks = static_cast<int64_t>(g.num_tiles) * kUpdPerTile;
+  const dim3 grid(static_cast<unsigned>(chunks < kMaxGrid ? chunks : kMaxGrid)), block(kBlock);
   const bool pow2 = (g.W & (g.W - 1)) == 0;
   if (bf16) {
     if (pow2) hipLaunchKernelGGL((warmup_kernel<uint16_t, true>), grid, block, 0, s, g, a);
