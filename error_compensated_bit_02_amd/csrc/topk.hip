@@ -790,9 +790,20 @@ template <bool kPow2>
 __global__ __launch_bounds__(kBlock) void topk_average(TopkArgs a, int W) {
   const float wf = static_cast<float>(W);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  constexpr int kGroup = 8;   // workers whose loads are issued together
   for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < a.K; j += stride) {
     float acc = 0.0f;
-    for (int w = 0; w < W; ++w) acc = acc + a.values[static_cast<size_t>(w) * a.K + j];
+    for (int w0 = 0; w0 < W; w0 += kGroup) {
+      float x[kGroup];
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k)
+        x[k] = w0 + k < W ? a.values[static_cast<size_t>(w0 + k) * a.K + j] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < kGroup; ++k) {
+        if (w0 + k >= W) break;
+        acc = acc + x[k];
+      }
+    }
     a.average[j] = kPow2 ? acc * (1.0f / wf) : acc / wf;
   }
 }
