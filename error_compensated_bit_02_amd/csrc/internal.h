@@ -57,6 +57,24 @@ inline size_t partials_count(int W, int num_tiles) {
   return static_cast<size_t>(W + 1) * static_cast<size_t>(num_tiles);
 }
 
+// The residual worker pass works in chunks: one workgroup per (chunk of
+// kChunk elements of a tile, worker), lane l of wavefront v owning element
+// kChunk/kWaves * v + 64*c + l of the chunk, and one partial per chunk:
+// W rows of num_tiles * kChunksPerTile pairs (chunks past a tile's end hold 0).
+constexpr int kChunk = 1024;
+constexpr int kChunksPerTile = kTile / kChunk;
+static_assert(kTile % kChunk == 0 && kChunk % (64 * kWaves) == 0, "chunk shape");
+inline size_t chunk_partials_count(int W, int num_tiles) {
+  return static_cast<size_t>(W) * static_cast<size_t>(num_tiles) * kChunksPerTile;
+}
+// Whether the residual worker pass runs in chunks: with fp32 gradients and
+// at most 8 workers (faster there, slower with bf16 gradients or with 32
+// and more workers, measured on MI355X), when its grid fits the device's
+// limit of 2^32 - 1 work-items per dimension.  Otherwise the tiled pass.
+inline bool use_chunked_worker(int W, bool bf16, int64_t num_tiles) {
+  return !bf16 && W <= 8 && num_tiles * kChunksPerTile <= 0xffffffffLL / kBlock;
+}
+
 enum Kind {
   K_WORKER_PASS1 = 0,
   K_SCALE_FINALIZE,
@@ -90,7 +108,9 @@ struct WorkerArgs {
   const float *scale_w;      // [W][T]: this step's (strict errors) or the previous step's (residual)
   const uint64_t *packed_s;  // [Nw] previous server message (residual)
   const float *scale_s;      // [T]  previous server scales (residual)
-  double2 *partials;
+  double2 *partials;         // per-tile partials (strict passes)
+  double2 *chunk_partials;   // per-chunk partials (residual passes, chunked)
+  bool chunked;              // residual passes in chunks (use_chunked_worker)
   int w0, w1;                // workers [w0, w1)
   int wgroup;                // workers per workgroup (see worker_group_size)
   float c1, c2;
@@ -188,11 +208,12 @@ enum class TopkStage { kSelect, kGather, kAverage };
 void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s);
 
 void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerArgs &a, hipStream_t s);
-// Scales of rows [row0, row0 + nrows) of the partials over `count` items
-// whose tile ranges are begin[i] .. begin[i+1]-1 and sizes numel[i]; row r's
-// scale of item i goes to out[(r - row0) * count + i].
-void launch_scale_finalize(const Geometry &g, const double2 *partials, int row0, int nrows,
-                           const int32_t *begin, const int64_t *numel, int count, float *out,
+// Scales of rows [row0, row0 + nrows) of the partials (rows of `cols` pairs,
+// `per` pairs per tile) over `count` items whose tile ranges are begin[i] ..
+// begin[i+1]-1 and sizes numel[i]; row r's scale of item i goes to
+// out[(r - row0) * count + i].
+void launch_scale_finalize(const Geometry &g, const double2 *partials, int64_t cols, int per, int row0,
+                           int nrows, const int32_t *begin, const int64_t *numel, int count, float *out,
                            hipStream_t s);
 void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s);
 // with_ratio: p -= lr * (ratio[t] * u), u = m / (sqrt(v) + eps) (+ wd * p)

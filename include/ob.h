@@ -44,8 +44,10 @@
  * Ownership.  The caller owns every buffer passed in: device memory (HBM)
  * pointers, each aligned to 16 bytes.  The library owns only the context and
  * its scratch: a tile table, server-piece tables and per-tile partial sums
- * (allocated in ob_init), and the CLT-k codec's keys, histograms and per-tile
- * counts (allocated in ob_cltk_configure); ob_destroy frees both.
+ * (per 1024-element chunk for the residual worker pass with fp32 gradients
+ * and at most 8 workers) (allocated in ob_init), and the CLT-k codec's
+ * histograms, candidate lists, masks and per-tile counts (allocated in
+ * ob_cltk_configure); ob_destroy frees both.
  *
  * Streams.  Every device call enqueues its kernels on the given stream (a
  * hipStream_t; NULL means the null stream) and returns without waiting.  A

@@ -35,6 +35,17 @@ def test_residual_ragged_w3():
     assert rep.exact_floats == rep.total_floats
 
 
+@pytest.mark.parametrize("W", [8, 9])
+def test_residual_ragged_f32_either_worker_pass(W):
+    """fp32 gradients with up to 8 workers take the chunked worker pass (one
+    workgroup per 1024-element chunk and worker, per-chunk partials), 9 and
+    more the tiled one; both must match the oracle exactly."""
+    wl = _wl(f"ragged_w{W}_residual", RAGGED, W, steps=4)
+    rep = parity_run(wl, wl.steps, residual=True)
+    _report(wl.name, rep)
+    assert rep.exact_floats == rep.total_floats
+
+
 def test_residual_ragged_bf16_w8():
     wl = _wl("ragged_bf16_w8_residual", RAGGED, 8, dtype="bf16", steps=4, g_sigma=5e-4)
     rep = parity_run(wl, wl.steps, residual=True)
