@@ -7,8 +7,9 @@
 
 namespace ob {
 
-// One workgroup handles one tile: kTile consecutive elements of one tensor
-// (a tensor's last tile may be shorter; no tile spans two tensors).  Each of
+// One workgroup handles one tile (or one chunk of one; see kChunk): kTile
+// consecutive elements of one tensor (a tensor's last tile may be shorter;
+// no tile spans two tensors).  Each of
 // the kWaves wavefronts owns kSub consecutive elements of the tile, and lane
 // l of a wavefront owns element 64*c + l of its range for c < kPerLane, so a
 // wavefront-wide ballot over one c yields one packed sign word in natural

@@ -18,7 +18,12 @@
 // (bit l = element 64 c + l), so packing costs one compare per element.
 // Sums of squares are reduced per wavefront, parked in LDS, folded per tile
 // in a fixed order (two barriers per tile, none per worker) and per tensor by
-// scale_finalize.
+// scale_finalize.  Three passes take their tile in chunks of 1024 elements
+// instead, one workgroup per chunk (lane l of wavefront v owning element
+// 256 v + 64 c + l of the chunk): the parameter update, the warmup step and,
+// with fp32 gradients and at most 8 workers, the residual worker pass (one
+// workgroup per (chunk, worker), one partial sum per chunk).  On MI355X a
+// stream runs faster in such 4 KB workgroups taken in address order.
 //
 // Two forms of the state between steps:
 //   strict    err_w / err_s hold the errors and m the momentum (two passes
