@@ -44,3 +44,15 @@ def test_algorithmic_bytes_closed_forms():
     assert kb["server_residual"] + kb["update_residual"] + kb["worker_residual"] == 118.375
     cl = bench.cltk_bytes_per_element(bl, 0.01)
     assert cl["cltk_select"] == 8.0 and abs(cl["cltk_gather"] - 96.36) < 1e-9
+
+
+def test_more_than_one_gpu_is_refused():
+    """One GPU holds every simulated worker: --gpus N > 1 exits with a message
+    before touching a device."""
+    import subprocess
+    import sys
+    root = bench.ROOT
+    r = subprocess.run([sys.executable, f"{root}/bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr + r.stdout
