@@ -7,7 +7,8 @@
 // and every worker sends its x at the leader's k largest positions.  The
 // selection is exact: the k-th largest key (the bit pattern of |x|, which
 // orders non-negative floats) is found by a radix select with 11, 11 and
-// 9-bit digits (per-tile LDS histograms added into per-tensor histograms).
+// 9-bit digits (LDS histograms per tile, per 64 tiles or per wavefront,
+// added into per-tensor histograms).
 // Pass 1 reads the leader's memory and gradient once: the first digit's
 // histogram, and for a window of first-digit bins around the previous
 // exchange's threshold, per tile, a bit mask of the keys above the window and
