@@ -46,6 +46,18 @@ def test_residual_ragged_f32_either_worker_pass(W):
     assert rep.exact_floats == rep.total_floats
 
 
+@pytest.mark.parametrize("W,dtype", [(1, "f32"), (2, "f32"), (16, "f32"), (3, "bf16")])
+def test_residual_ragged_more_worker_counts(W, dtype):
+    """One and two workers (chunked worker pass; W = 1 and 2 are powers of two,
+    so the server multiplies by 1/W), sixteen (tiled, one group of 16) and bf16
+    gradients with three (tiled)."""
+    sigma = 5e-4 if dtype == "bf16" else 1e-3
+    wl = _wl(f"ragged_w{W}_{dtype}_residual", RAGGED, W, dtype=dtype, steps=3, g_sigma=sigma)
+    rep = parity_run(wl, wl.steps, residual=True)
+    _report(wl.name, rep)
+    assert rep.exact_floats == rep.total_floats
+
+
 def test_residual_ragged_bf16_w8():
     wl = _wl("ragged_bf16_w8_residual", RAGGED, 8, dtype="bf16", steps=4, g_sigma=5e-4)
     rep = parity_run(wl, wl.steps, residual=True)
