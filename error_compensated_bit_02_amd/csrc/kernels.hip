@@ -381,9 +381,9 @@ __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
   const int r = static_cast<int>(id / count);
   const int item = static_cast<int>(id % count);
   const double2 *row = partials + static_cast<size_t>(row0 + r) * cols;
-  // four independent chains per lane, their loads issued together, then
+  // eight independent chains per lane, their loads issued together, then
   // folded in a fixed order
-  constexpr int kChains = 4;
+  constexpr int kChains = 8;
   double ch[kChains], cl[kChains];
 #pragma unroll
   for (int k = 0; k < kChains; ++k) ch[k] = cl[k] = 0.0;
