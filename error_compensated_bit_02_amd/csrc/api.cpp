@@ -48,7 +48,7 @@ struct ob_ctx {
   void *scratch = nullptr;         // one device allocation: tiles | tile_begin | numel | partials
   ob::Geometry geo{};
   double2 *partials = nullptr;     // (W+1) x num_tiles
-  double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile (residual worker pass)
+  double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile, when use_chunked_worker
   bool profiling = false;
   std::vector<EventPair> pending[ob::K_NUM_KINDS];
   std::vector<EventPair> pool;
@@ -353,7 +353,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->geo.piece_numel = c->d_piece_numel;
   c->d_ratio = reinterpret_cast<float *>(pieces + b_pieces);
   c->partials = reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio);
-  c->chunk_partials = reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio + b_part);
+  c->chunk_partials = b_cpart ? reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio + b_part) : nullptr;
   c->geo.num_tiles = c->num_tiles;
   c->geo.T = c->T;
   c->geo.W = c->W;
