@@ -48,7 +48,7 @@ struct ob_ctx {
   void *scratch = nullptr;         // one device allocation: tiles | tile_begin | numel | partials
   ob::Geometry geo{};
   double2 *partials = nullptr;     // (W+1) x num_tiles
-  double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile, when use_chunked_worker
+  double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile (residual worker pass)
   bool profiling = false;
   std::vector<EventPair> pending[ob::K_NUM_KINDS];
   std::vector<EventPair> pool;
@@ -119,7 +119,6 @@ ob::WorkerArgs worker_args(ob_ctx *c, int w0, int w1, const void *grads, const f
   a.scale_s = scale_s;
   a.partials = c->partials;
   a.chunk_partials = c->chunk_partials;
-  a.chunked = ob::use_chunked_worker(c->W, c->bf16, c->num_tiles);
   a.w0 = w0;
   a.w1 = w1;
   a.wgroup = ob::worker_group_size(w1 - w0, c->num_tiles);
@@ -277,11 +276,12 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->N = off[num_tensors];
 
   // The largest launches must fit the device's grid limit: (worker group,
-  // tile) workgroups, and the scale finalize's one wavefront per (worker,
-  // tensor).  (The chunked residual worker pass is used only where it fits.)
+  // tile) workgroups of the strict worker passes, (chunk, worker) workgroups
+  // of the residual one (chunks along x, workers along y), and the scale
+  // finalize's one wavefront per (worker, tensor).
   int64_t nt = 0;
   for (int32_t t = 0; t < num_tensors; ++t) nt += (numel[t] + ob::kTile - 1) / ob::kTile;
-  if (nt > ob::kMaxGrid) {
+  if (nt * ob::kChunksPerTile > ob::kMaxGrid) {
     delete c;
     return OB_ERR_INVALID;
   }
@@ -319,8 +319,8 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   const size_t b_ratio = up(c->numel.size() * sizeof(float));
   const size_t b_part =
       up(ob::partials_count(num_workers, static_cast<int>(tiles.size())) * sizeof(double2));
-  const size_t b_cpart = ob::use_chunked_worker(num_workers, grad_dtype == OB_GRAD_BF16, nt)
-      ? up(ob::chunk_partials_count(num_workers, static_cast<int>(tiles.size())) * sizeof(double2)) : 0;
+  const size_t b_cpart =
+      up(ob::chunk_partials_count(num_workers, static_cast<int>(tiles.size())) * sizeof(double2));
   std::vector<unsigned char> host(b_tiles + b_begin + b_numel, 0);
   std::copy(reinterpret_cast<const unsigned char *>(tiles.data()),
             reinterpret_cast<const unsigned char *>(tiles.data() + tiles.size()), host.data());
@@ -353,7 +353,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->geo.piece_numel = c->d_piece_numel;
   c->d_ratio = reinterpret_cast<float *>(pieces + b_pieces);
   c->partials = reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio);
-  c->chunk_partials = b_cpart ? reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio + b_part) : nullptr;
+  c->chunk_partials = reinterpret_cast<double2 *>(pieces + b_pieces + b_ratio + b_part);
   c->geo.num_tiles = c->num_tiles;
   c->geo.T = c->T;
   c->geo.W = c->W;
@@ -463,12 +463,8 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   });
   if (r) return r;
   r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    if (wa.chunked)
-      ob::launch_scale_finalize(g, c->chunk_partials, static_cast<int64_t>(g.num_tiles) * ob::kChunksPerTile,
-                                ob::kChunksPerTile, 0, c->W, g.tile_begin, g.numel, c->T, scale_w, s);
-    else
-      ob::launch_scale_finalize(g, c->partials, g.num_tiles, 1, 0, c->W, g.tile_begin, g.numel, c->T,
-                                scale_w, s);
+    ob::launch_scale_finalize(g, c->chunk_partials, static_cast<int64_t>(g.num_tiles) * ob::kChunksPerTile,
+                              ob::kChunksPerTile, 0, c->W, g.tile_begin, g.numel, c->T, scale_w, s);
   });
   if (r) return r;
   const ob::ServerArgs sa = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);

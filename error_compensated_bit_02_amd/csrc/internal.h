@@ -68,13 +68,6 @@ static_assert(kTile % kChunk == 0 && kChunk % (64 * kWaves) == 0, "chunk shape")
 inline size_t chunk_partials_count(int W, int num_tiles) {
   return static_cast<size_t>(W) * static_cast<size_t>(num_tiles) * kChunksPerTile;
 }
-// Whether the residual worker pass runs in chunks: with fp32 gradients and
-// at most 8 workers (faster there, slower with bf16 gradients or with 32
-// and more workers, measured on MI355X), when its grid fits the device's
-// limit of 2^32 - 1 work-items per dimension.  Otherwise the tiled pass.
-inline bool use_chunked_worker(int W, bool bf16, int64_t num_tiles) {
-  return !bf16 && W <= 8 && num_tiles * kChunksPerTile <= 0xffffffffLL / kBlock;
-}
 
 enum Kind {
   K_WORKER_PASS1 = 0,
@@ -110,14 +103,14 @@ struct WorkerArgs {
   const uint64_t *packed_s;  // [Nw] previous server message (residual)
   const float *scale_s;      // [T]  previous server scales (residual)
   double2 *partials;         // per-tile partials (strict passes)
-  double2 *chunk_partials;   // per-chunk partials (residual passes, chunked)
-  bool chunked;              // residual passes in chunks (use_chunked_worker)
+  double2 *chunk_partials;   // per-chunk partials (residual passes)
   int w0, w1;                // workers [w0, w1)
-  int wgroup;                // workers per workgroup (see worker_group_size)
+  int wgroup;                // workers per workgroup of the strict passes (see worker_group_size)
   float c1, c2;
 };
 
-// Workers handled by one workgroup of a worker pass.  At most kMaxGroup, so
+// Workers handled by one workgroup of a tiled worker pass (the strict form's
+// two passes and the CLT-k gather).  At most kMaxGroup, so
 // the workgroups resident at once stream few rows; fewer when the tile count
 // alone would leave the launch short of kMinBlocks workgroups (many small
 // launches of a small list would leave most of the 256 CUs idle at the tail).

@@ -20,10 +20,10 @@
 // in a fixed order (two barriers per tile, none per worker) and per tensor by
 // scale_finalize.  Three passes take their tile in chunks of 1024 elements
 // instead, one workgroup per chunk (lane l of wavefront v owning element
-// 256 v + 64 c + l of the chunk): the parameter update, the warmup step and,
-// with fp32 gradients and at most 8 workers, the residual worker pass (one
-// workgroup per (chunk, worker), one partial sum per chunk).  On MI355X a
-// stream runs faster in such 4 KB workgroups taken in address order.
+// 256 v + 64 c + l of the chunk): the parameter update, the warmup step and
+// the residual worker pass (one workgroup per (chunk, worker), one partial
+// sum per chunk).  On MI355X a stream runs faster in such 4 KB workgroups
+// taken in address order.
 //
 // Two forms of the state between steps:
 //   strict    err_w / err_s hold the errors and m the momentum (two passes
@@ -179,26 +179,21 @@ __device__ __forceinline__ float signed_scale(uint64_t words, int c, float s) {
 //   kResidFirst  residual, first step: as kPass1 from stored e and m, and x is stored
 //   kResid       residual: e = x_prev - s_prev*sign(x_prev), m = previous server
 //                message; then as kResidFirst
+// The strict passes run in tiles (worker_kernel), the residual ones in chunks
+// (worker_chunk_kernel).
 // ---------------------------------------------------------------------------
 enum { kPass1 = 0, kPass2 = 1, kResidFirst = 2, kResid = 3 };
 
 template <int kMode, typename G, bool kFull>
 __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, const WorkerArgs &a,
                                             int w_lo, int w_hi, const PartialSink &sink) {
+  static_assert(kMode == kPass1 || kMode == kPass2, "the tiled worker pass is the strict form's");
   const Lanes ln = lanes_of<kFull>(tl);
   const int t = tl.tensor;
   float mr[kPerLane];
-  if (kMode == kResid) {
-    const float ss = a.scale_s[g.tile_piece[sink.tile]];
-    const uint64_t words = load_words<kFull>(a.packed_s + (ln.base >> 6), ln);
 #pragma unroll
-    for (int c = 0; c < kPerLane; ++c)
-      mr[c] = in_tile<kFull>(tl, ln, c) ? signed_scale(words, c, ss) : 0.0f;
-  } else {
-#pragma unroll
-    for (int c = 0; c < kPerLane; ++c)
-      mr[c] = in_tile<kFull>(tl, ln, c) ? a.m[ln.base + 64 * c + ln.lane] : 0.0f;
-  }
+  for (int c = 0; c < kPerLane; ++c)
+    mr[c] = in_tile<kFull>(tl, ln, c) ? a.m[ln.base + 64 * c + ln.lane] : 0.0f;
 
   const G *grads = static_cast<const G *>(a.grads) + ln.base + ln.lane;
   float gv[kPerLane], ev[kPerLane];
@@ -213,11 +208,10 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
     }
   };
   for (int w = w_lo; w < w_hi; ++w) {
-    float *ew = a.err_w + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
-    // kPass2: this step's scale; kResid: the previous step's scale
-    const float s = (kMode == kPass2 || kMode == kResid) ? a.scale_w[static_cast<size_t>(w) * g.T + t] : 0.0f;
     load(w, gv, ev);
     if (kMode == kPass2) {
+      float *ew = a.err_w + static_cast<size_t>(w) * g.N + ln.base + ln.lane;
+      const float s = a.scale_w[static_cast<size_t>(w) * g.T + t];   // this step's scale
 #pragma unroll
       for (int c = 0; c < kPerLane; ++c) {
         const float mw = a.c1 * mr[c] + a.c2 * gv[c];
@@ -231,17 +225,15 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
       const bool ok = in_tile<kFull>(tl, ln, c);
-      const float e = (kMode == kResid) ? onebit_error(ev[c], s) : ev[c];
       const float mw = a.c1 * mr[c] + a.c2 * gv[c];
-      const float x = ok ? mw + e : 0.0f;
+      const float x = ok ? mw + ev[c] : 0.0f;
       const uint64_t bal = __ballot(ok && x >= 0.0f);
       if (ln.lane == c) word = bal;
       dd_accumulate(hi, lo, x);  // lanes outside the tile hold x = 0 and add nothing
-      if (kMode != kPass1 && ok) ew[64 * c] = x;
     }
     // Non-temporal: the sign words are read only by the server pass.  Cached,
-    // one 256-byte row piece per worker beside the x rows slowed this pass by
-    // ~7% at W = 64 (measured; no effect at W = 8).
+    // one 256-byte row piece per worker beside the other rows slowed a tiled
+    // worker pass by ~7% at W = 64 (measured; no effect at W = 8).
     if (ln.lane < ln.nwords)
       __builtin_nontemporal_store(word, &a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane]);
     const int slot = (w - w_lo) % kFlushRows;
@@ -279,10 +271,11 @@ __global__ __launch_bounds__(kBlock) void worker_kernel(Geometry g, WorkerArgs a
 // pieces of it go to consecutive XCDs (workgroups are dispatched to the XCDs
 // in turn).  Sums of squares go to one partial per (worker, chunk).
 //
-// Used for fp32 gradients and at most 8 workers (use_chunked_worker): there,
-// in fresh processes on MI355X, 5.4-5.6 ms per BERT-Large-sized step against
-// 5.8-6.3 ms for the tiled pass; with bf16 gradients or 32 and 64 workers
-// it was 2-6% slower than the tiled pass.
+// On MI355X this shape beat a tiled pass that loops over the workers of each
+// 8192-element tile at every worker count and gradient type measured, and it
+// varies far less between processes: at a BERT-Large-sized list with 8
+// workers 5.4-5.6 ms against 5.8-6.3 ms in fresh processes, at a
+// BERT-base-sized list with 64 workers 13.9-14.1 ms against 15.2-16.7 ms.
 // ---------------------------------------------------------------------------
 constexpr int kChunkSub = kChunk / kWaves;   // elements per wavefront
 constexpr int kChunkPerLane = kChunkSub / 64;
@@ -797,7 +790,7 @@ __global__ __launch_bounds__(kBlock) void zero_errors_kernel(Geometry g, float *
 template <typename G>
 void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStream_t s) {
   const dim3 block(kBlock);
-  if (a.chunked && (mode == kResidFirst || mode == kResid)) {
+  if (mode == kResidFirst || mode == kResid) {
     const dim3 grid(static_cast<unsigned>(g.num_tiles) * kChunksPerTile, static_cast<unsigned>(a.w1 - a.w0));
     if (mode == kResidFirst)
       hipLaunchKernelGGL((worker_chunk_kernel<G, kResidFirst>), grid, block, 0, s, g, a);
@@ -807,12 +800,10 @@ void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStr
   }
   const int groups = (a.w1 - a.w0 + a.wgroup - 1) / a.wgroup;
   const dim3 grid(static_cast<unsigned>(g.num_tiles) * static_cast<unsigned>(groups));
-  switch (mode) {
-    case kPass1: hipLaunchKernelGGL((worker_kernel<G, kPass1>), grid, block, 0, s, g, a); break;
-    case kPass2: hipLaunchKernelGGL((worker_kernel<G, kPass2>), grid, block, 0, s, g, a); break;
-    case kResidFirst: hipLaunchKernelGGL((worker_kernel<G, kResidFirst>), grid, block, 0, s, g, a); break;
-    default: hipLaunchKernelGGL((worker_kernel<G, kResid>), grid, block, 0, s, g, a); break;
-  }
+  if (mode == kPass1)
+    hipLaunchKernelGGL((worker_kernel<G, kPass1>), grid, block, 0, s, g, a);
+  else
+    hipLaunchKernelGGL((worker_kernel<G, kPass2>), grid, block, 0, s, g, a);
 }
 
 }  // namespace

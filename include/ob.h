@@ -43,9 +43,9 @@
  *
  * Ownership.  The caller owns every buffer passed in: device memory (HBM)
  * pointers, each aligned to 16 bytes.  The library owns only the context and
- * its scratch: a tile table, server-piece tables and per-tile partial sums
- * (per 1024-element chunk for the residual worker pass with fp32 gradients
- * and at most 8 workers) (allocated in ob_init), and the CLT-k codec's
+ * its scratch: a tile table, server-piece tables and partial sums per tile
+ * and, for the residual worker pass, per 1024-element chunk (allocated in
+ * ob_init), and the CLT-k codec's
  * histograms, candidate lists, masks and per-tile counts (allocated in
  * ob_cltk_configure); ob_destroy frees both.
  *
@@ -101,7 +101,8 @@ int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off);
  * with synchronous copies.  OB_ERR_INVALID also when a launch over the list
  * would exceed the device's grid limit (2^32 - 1 work-items, i.e. 16,777,215
  * workgroups of 256): the (worker group, tile) grid of 8192-element tiles,
- * or one wavefront per (worker, tensor) for the scales.  OB_ERR_NOMEM when the
+ * the 1024-element chunks of the residual worker pass, or one wavefront per
+ * (worker, tensor) for the scales.  OB_ERR_NOMEM when the
  * scratch cannot be allocated.  Blocking calls of this library: ob_init,
  * ob_destroy, ob_set_server_chunks, ob_cltk_configure and ob_profile_read;
  * every other call only enqueues work on the given stream. */

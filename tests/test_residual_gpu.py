@@ -36,10 +36,11 @@ def test_residual_ragged_w3():
 
 
 @pytest.mark.parametrize("W", [8, 9])
-def test_residual_ragged_f32_either_worker_pass(W):
-    """fp32 gradients with up to 8 workers take the chunked worker pass (one
-    workgroup per 1024-element chunk and worker, per-chunk partials), 9 and
-    more the tiled one; both must match the oracle exactly."""
+def test_residual_ragged_f32_w8_w9(W):
+    """The residual worker pass (one workgroup per 1024-element chunk and
+    worker, per-chunk partials) with 8 workers and with 9, where the server
+    divides by W instead of multiplying by 1/W; both must match the oracle
+    exactly."""
     wl = _wl(f"ragged_w{W}_residual", RAGGED, W, steps=4)
     rep = parity_run(wl, wl.steps, residual=True)
     _report(wl.name, rep)
@@ -48,9 +49,8 @@ def test_residual_ragged_f32_either_worker_pass(W):
 
 @pytest.mark.parametrize("W,dtype", [(1, "f32"), (2, "f32"), (16, "f32"), (3, "bf16")])
 def test_residual_ragged_more_worker_counts(W, dtype):
-    """One and two workers (chunked worker pass; W = 1 and 2 are powers of two,
-    so the server multiplies by 1/W), sixteen (tiled, one group of 16) and bf16
-    gradients with three (tiled)."""
+    """One and two workers (W = 1 and 2 are powers of two, so the server
+    multiplies by 1/W), sixteen, and bf16 gradients with three."""
     sigma = 5e-4 if dtype == "bf16" else 1e-3
     wl = _wl(f"ragged_w{W}_{dtype}_residual", RAGGED, W, dtype=dtype, steps=3, g_sigma=sigma)
     rep = parity_run(wl, wl.steps, residual=True)
