@@ -112,6 +112,7 @@ def test_materialize_in_place_then_strict_continues():
 
 @pytest.mark.parametrize("name,sample", [
     ("bert_large", ["layer0.attn.q.bias", "layer3.attn.v.weight", "layer23.ln2.gamma", "embed.position"]),
+    ("bert_base_w64", ["layer0.attn.q.bias", "layer0.attn.k.weight", "layer11.ln2.beta"]),
     ("resnet50_w32", ["stem.conv", "stage2.block1.reduce.bn.beta", "fc.bias"]),
     ("gpt_1p3b_bf16", ["h0.ln1.gamma", "h5.attn.out.bias", "ln_f.beta"]),
 ])
