@@ -84,7 +84,8 @@ int check_ptrs(const P *...ps) {
   return st;
 }
 
-// Brackets one launch with events when profiling is on.
+// Brackets one launch with events when profiling is on.  On a failure the
+// event pair goes back to the pool.
 template <typename F>
 int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
   EventPair ev;
@@ -92,18 +93,28 @@ int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
     if (!c->pool.empty()) {
       ev = c->pool.back();
       c->pool.pop_back();
-    } else if (hipEventCreate(&ev.start) != hipSuccess || hipEventCreate(&ev.stop) != hipSuccess) {
+    } else {
+      if (hipEventCreate(&ev.start) != hipSuccess) return OB_ERR_DEVICE;
+      if (hipEventCreate(&ev.stop) != hipSuccess) {
+        (void)hipEventDestroy(ev.start);
+        return OB_ERR_DEVICE;
+      }
+    }
+    if (hipEventRecord(ev.start, s) != hipSuccess) {
+      c->pool.push_back(ev);
       return OB_ERR_DEVICE;
     }
-    if (hipEventRecord(ev.start, s) != hipSuccess) return OB_ERR_DEVICE;
   }
   launch();
-  if (hipGetLastError() != hipSuccess) return OB_ERR_DEVICE;
+  const bool launched = hipGetLastError() == hipSuccess;
   if (c->profiling) {
-    if (hipEventRecord(ev.stop, s) != hipSuccess) return OB_ERR_DEVICE;
+    if (!launched || hipEventRecord(ev.stop, s) != hipSuccess) {
+      c->pool.push_back(ev);
+      return OB_ERR_DEVICE;
+    }
     c->pending[kind].push_back(ev);
   }
-  return OB_OK;
+  return launched ? OB_OK : OB_ERR_DEVICE;
 }
 
 ob::WorkerArgs worker_args(ob_ctx *c, int w0, int w1, const void *grads, const float *m,
@@ -258,7 +269,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   if (num_workers < 1 || num_workers > 4096) return OB_ERR_INVALID;
   if (grad_dtype != OB_GRAD_F32 && grad_dtype != OB_GRAD_BF16) return OB_ERR_INVALID;
   if (!std::isfinite(beta1) || beta1 < 0.0 || beta1 >= 1.0) return OB_ERR_INVALID;
-  if (!std::isfinite(eps) || eps <= 0.0) return OB_ERR_INVALID;
+  if (!std::isfinite(eps) || !(static_cast<float>(eps) > 0.0f)) return OB_ERR_INVALID;   // eps > 0 in fp32
   std::vector<int64_t> off(static_cast<size_t>(num_tensors > 0 ? num_tensors : 0) + 1);
   const int lay = ob_layout(num_tensors, numel, off.data());
   if (lay != OB_OK) return lay;
@@ -579,8 +590,11 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
   a.K = k_off[T];
   const std::vector<uint32_t> no_prediction(T, 0xffffffffu);   // the first exchange has none
   if (hipMemcpy(at[0], k_off.data(), (T + 1) * 8, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(at[8], no_prediction.data(), T * 4, hipMemcpyHostToDevice) != hipSuccess)
+      hipMemcpy(at[8], no_prediction.data(), T * 4, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(c->topk_scratch);   // leave the codec unconfigured
+    c->topk_scratch = nullptr;
     return OB_ERR_DEVICE;
+  }
   c->k_off = k_off;
   if (k_total) *k_total = a.K;
   return OB_OK;

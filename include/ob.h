@@ -96,7 +96,8 @@ int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off);
 
 /* Creates a context for T tensors of numel[] elements (host array, copied),
  * 1 <= W <= 4096 simulated workers, gradients of grad_dtype, and the fixed
- * hyper-parameters beta1 (momentum, in [0, 1)) and eps (> 0).  Allocates the
+ * hyper-parameters beta1 (momentum, in [0, 1)) and eps (> 0 also once rounded
+ * to fp32, the precision the kernels use it in).  Allocates the
  * context's device scratch on the current HIP device and uploads its tables
  * with synchronous copies.  OB_ERR_INVALID also when a launch over the list
  * would exceed the device's grid limit (2^32 - 1 work-items, i.e. 16,777,215

@@ -80,6 +80,7 @@ def test_init_argument_checks_fail_before_device_work(lib):
     assert lib.ob_init(ctypes.byref(ctx), 2, (ctypes.c_int64 * 2)(100, 0), 4, 0, 0.9, 1e-8) == 1
     assert lib.ob_init(None, 2, n, 4, 0, 0.9, 1e-8) == 1
     assert lib.ob_init(ctypes.byref(ctx), 2, n, 4097, 0, 0.9, 1e-8) == 1    # W > 4096
+    assert lib.ob_init(ctypes.byref(ctx), 2, n, 4, 0, 0.9, 1e-50) == 1     # eps rounds to 0 in fp32
     assert ctx.value is None
 
 
