@@ -1,0 +1,220 @@
+// Plain, single-threaded C++ oracle of one compression-phase step of 1-bit
+// Adam, for one tensor.
+//
+// TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the
+// build entry module and the CPU-baseline leg of the benchmark load this
+// library.  It shares no code with the HIP library (no header, no helper, no
+// table) and the HIP library never loads it.
+//
+// Source pages: the nubint.ai review of "1-bit Adam: Communication Efficient
+// Large-Scale Training with Adam's Convergence Speed" (Tang, Gan et al.).  In
+// the compression phase, Adam's variance is frozen and used as a fixed
+// preconditioner (Abstract; Proposed method, bullet 2), and training runs as
+// momentum SGD whose momentum is sent with error-compensated 1-bit
+// compression (One-line summary; Proposed method, bullets 1 and 3) through a
+// collective (bullet 4), here a local average of the W workers' messages
+// followed by a server-side re-compression with its own error buffer.
+//
+// The pages give no formulas.  The readings taken (the same as the numpy
+// oracle's R1-R9):
+//   scale     s = fp32( sqrt64( fl64(exact sum of x_i^2) / n ) )       (R1)
+//   sign bit  x >= 0 gives 1 (also for -0); NaN gives 0                (R2)
+//   layout    uint64 words, bit k of word j is element 64 j + k;
+//             bits past the tensor's end are 0                         (R3)
+//   one scale per (worker, tensor), one for the server                 (R4)
+//   momentum  m_w = c1*m + c2*g_w, c1 = fp32(beta1),
+//             c2 = fp32(1 - beta1) with the complement in double      (R5)
+//   average   ascending fp32 sum over workers from +0, then / W        (R6)
+//   momentum after the step: the server's reconstruction               (R7)
+//   update    p - lr*(m/(sqrt(v)+eps)), fp32, correctly rounded       (R8)
+//   a NaN or Inf anywhere in a tensor makes its scale NaN              (R9)
+// Every fp32 product and sum below is its own statement and the file is
+// compiled with -ffp-contract=off, so each rounds once.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// exact sum of squares of fp32 values (R1)
+//
+// |x| = M * 2^(k - 149) with M < 2^24 an integer and 0 <= k <= 253
+// (normal: M = 2^23 + fraction, k = biased exponent - 1; subnormal: M =
+// fraction, k = 0).  So x^2 = M^2 * 2^(2k - 298) with M^2 < 2^48, and
+// 2^298 * sum x^2 = sum over k of B_k * 2^(2k), B_k = sum of M^2 over the
+// elements with exponent index k (below 2^88 for up to 2^40 terms: exact in
+// 128 bits).  The total is an integer below 2^(506 + 88): ten 64-bit limbs
+// hold it exactly.
+// ---------------------------------------------------------------------------
+constexpr int kLimbs = 10;
+
+struct BigSum {
+  uint64_t limb[kLimbs] = {};
+
+  // += v * 2^shift
+  void add(uint64_t v, int shift) {
+    int i = shift / 64;
+    const int b = shift % 64;
+    unsigned __int128 part = static_cast<unsigned __int128>(v) << b;   // < 2^127
+    unsigned __int128 carry = 0;
+    while ((part != 0 || carry != 0) && i < kLimbs) {   // the total stays below 2^640
+      const unsigned __int128 t = static_cast<unsigned __int128>(limb[i]) +
+                                  static_cast<uint64_t>(part) + carry;
+      limb[i] = static_cast<uint64_t>(t);
+      carry = t >> 64;
+      part >>= 64;
+      ++i;
+    }
+  }
+
+  int top_bit() const {   // index of the highest set bit, -1 for zero
+    for (int i = kLimbs - 1; i >= 0; --i)
+      if (limb[i] != 0) return 64 * i + 63 - __builtin_clzll(limb[i]);
+    return -1;
+  }
+
+  bool bit(int pos) const { return pos >= 0 && ((limb[pos / 64] >> (pos % 64)) & 1u); }
+
+  bool any_below(int pos) const {   // any set bit at an index < pos
+    for (int i = 0; i < kLimbs && 64 * i < pos; ++i) {
+      const int hi = pos - 64 * i;   // bits [0, hi) of this limb count
+      const uint64_t mask = hi >= 64 ? ~0ull : ((1ull << hi) - 1);
+      if (limb[i] & mask) return true;
+    }
+    return false;
+  }
+
+  // this * 2^-298 rounded once to the nearest double, ties to even
+  double to_double() const {
+    const int h = top_bit();
+    if (h < 0) return 0.0;
+    uint64_t sig = 0;   // the 53 bits [h-52, h], or all of them when h <= 52
+    const int lo = h >= 52 ? h - 52 : 0;
+    for (int pos = h; pos >= lo; --pos) sig = (sig << 1) | (bit(pos) ? 1u : 0u);
+    if (h > 52) {
+      const bool half = bit(lo - 1);
+      const bool sticky = any_below(lo - 1);
+      if (half && (sticky || (sig & 1u))) sig += 1;   // may reach 2^53: still exact below
+    }
+    return std::ldexp(static_cast<double>(sig), lo - 298);
+  }
+};
+
+double exact_sum_of_squares(const float *x, int64_t n) {
+  unsigned __int128 bucket[254] = {};   // B_k
+  for (int64_t i = 0; i < n; ++i) {
+    if (!std::isfinite(x[i])) return std::nan("");
+    uint32_t u;
+    std::memcpy(&u, &x[i], 4);
+    const uint32_t biased = (u >> 23) & 0xFFu;
+    const uint32_t frac = u & 0x7FFFFFu;
+    const uint64_t M = biased > 0 ? (frac | 0x800000u) : frac;
+    const int k = biased > 0 ? static_cast<int>(biased) - 1 : 0;
+    bucket[k] += M * M;
+  }
+  BigSum acc;
+  for (int k = 0; k < 254; ++k) {
+    acc.add(static_cast<uint64_t>(bucket[k]), 2 * k);
+    acc.add(static_cast<uint64_t>(bucket[k] >> 64), 2 * k + 64);
+  }
+  return acc.to_double();
+}
+
+float onebit_scale(const float *x, int64_t n) {
+  const double S = exact_sum_of_squares(x, n);
+  const double q = S / static_cast<double>(n);
+  return static_cast<float>(std::sqrt(q));
+}
+
+bool sign_bit(float x) { return x >= 0.0f; }   // R2
+
+void pack_signs(const float *x, int64_t n, uint64_t *words) {
+  const int64_t nw = (n + 63) / 64;
+  for (int64_t j = 0; j < nw; ++j) words[j] = 0;
+  for (int64_t i = 0; i < n; ++i) words[i / 64] |= static_cast<uint64_t>(sign_bit(x[i])) << (i % 64);
+}
+
+bool unpacked_bit(const uint64_t *words, int64_t i) { return (words[i / 64] >> (i % 64)) & 1u; }
+
+// decompress of one element of a 1-bit message
+float decompressed(const uint64_t *words, float s, int64_t i) { return unpacked_bit(words, i) ? s : -s; }
+
+}  // namespace
+
+extern "C" {
+
+double ref_sum_of_squares(const float *x, int64_t n) { return exact_sum_of_squares(x, n); }
+
+float ref_scale(const float *x, int64_t n) { return onebit_scale(x, n); }
+
+void ref_pack_signs(const float *x, int64_t n, uint64_t *words) { pack_signs(x, n, words); }
+
+// One compression-phase step of one tensor of n elements with W workers.
+//   g        [W][n] fp32 gradients (bf16 gradients widened by the caller: exact)
+//   p, m     [n] parameters and the shared momentum, read and overwritten
+//   v        [n] frozen variance
+//   err_s    [n] server error, read and overwritten
+//   err_w    [W][n] worker errors, read and overwritten
+//   packed_w [W][ceil(n/64)] and scale_w [W]: the worker messages (written)
+//   packed_s [ceil(n/64)] and scale_s [1]: the server message (written)
+// Returns 0, or 1 for a bad argument (n < 1, W < 1, a null pointer).
+int ref_compression_step(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
+                         float *p, float *m, const float *v, float *err_s, float *err_w,
+                         uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s) {
+  if (n < 1 || W < 1 || !g || !p || !m || !v || !err_s || !err_w || !packed_w || !scale_w ||
+      !packed_s || !scale_s)
+    return 1;
+  const int64_t nw = (n + 63) / 64;
+  const float c1 = static_cast<float>(beta1);          // R5
+  const float c2 = static_cast<float>(1.0 - beta1);
+  std::vector<float> x(static_cast<size_t>(n));
+
+  // workers, each on its own: momentum, error feedback, 1-bit message, new error
+  for (int32_t w = 0; w < W; ++w) {
+    const float *gw = g + static_cast<size_t>(w) * n;
+    float *ew = err_w + static_cast<size_t>(w) * n;
+    uint64_t *words = packed_w + static_cast<size_t>(w) * nw;
+    for (int64_t i = 0; i < n; ++i) {
+      const float a = c1 * m[i];
+      const float b = c2 * gw[i];
+      const float mw = a + b;
+      x[i] = mw + ew[i];
+    }
+    const float s = onebit_scale(x.data(), n);
+    pack_signs(x.data(), n, words);
+    scale_w[w] = s;
+    for (int64_t i = 0; i < n; ++i) ew[i] = x[i] - decompressed(words, s, i);   // e = x - C(x)
+  }
+
+  // server: average of the decompressed messages, plus its own error
+  const float wf = static_cast<float>(W);
+  for (int64_t i = 0; i < n; ++i) {
+    float acc = 0.0f;
+    for (int32_t w = 0; w < W; ++w)
+      acc = acc + decompressed(packed_w + static_cast<size_t>(w) * nw, scale_w[w], i);
+    const float y = acc / wf;
+    x[i] = y + err_s[i];
+  }
+  const float ss = onebit_scale(x.data(), n);
+  pack_signs(x.data(), n, packed_s);
+  scale_s[0] = ss;
+
+  // server error, momentum = the server's reconstruction, preconditioned update
+  const float lr32 = static_cast<float>(lr);
+  const float eps32 = static_cast<float>(eps);
+  for (int64_t i = 0; i < n; ++i) {
+    const float mhat = decompressed(packed_s, ss, i);
+    err_s[i] = x[i] - mhat;
+    m[i] = mhat;
+    const float d = std::sqrt(v[i]) + eps32;
+    const float u = mhat / d;
+    const float step = lr32 * u;
+    p[i] = p[i] - step;
+  }
+  return 0;
+}
+
+}  // extern "C"

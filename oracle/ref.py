@@ -1,0 +1,116 @@
+"""ctypes front of the C++ oracle (oracle/onebit_ref.cpp): one compression-phase
+step of one tensor, plain and single-threaded.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the build
+entry module and the CPU-baseline leg of the benchmark may import this module.
+It shares nothing with the product path: the library is built from
+oracle/onebit_ref.cpp alone with the host compiler (g++), without floating-point
+contraction, and loads no part of the HIP library.
+
+The C++ oracle implements the same readings as oracle/onebit.py (R1-R9 in its
+header) in independent code: the exact sum of squares in a fixed-point integer
+accumulator instead of Python integers, the step as explicit loops.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import shutil
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "onebit_ref.cpp")
+LIB = os.path.join(HERE, "libonebit_ref.so")
+# -ffp-contract=off: every fp32 product and sum rounds once; no -ffast-math
+FLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+
+_lib: Optional[ctypes.CDLL] = None
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_u64p = np.ctypeslib.ndpointer(dtype=np.uint64, flags="C_CONTIGUOUS")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libonebit_ref.so next to its source; returns its path."""
+    cxx = os.environ.get("CXX") or shutil.which("g++") or "g++"
+    tmp = LIB + ".tmp"
+    cmd = [cxx, *FLAGS, "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"building the C++ oracle failed ({proc.returncode}):\n{proc.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def load() -> ctypes.CDLL:
+    """The C++ oracle library, built first if it is missing or older than its source."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        build()
+    lib = ctypes.CDLL(LIB)
+    lib.ref_sum_of_squares.restype = ctypes.c_double
+    lib.ref_sum_of_squares.argtypes = [_f32p, ctypes.c_int64]
+    lib.ref_scale.restype = ctypes.c_float
+    lib.ref_scale.argtypes = [_f32p, ctypes.c_int64]
+    lib.ref_pack_signs.restype = None
+    lib.ref_pack_signs.argtypes = [_f32p, ctypes.c_int64, _u64p]
+    lib.ref_compression_step.restype = ctypes.c_int
+    lib.ref_compression_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double,
+                                         ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p, _f32p,
+                                         _f32p, _u64p, _f32p, _u64p, _f32p]
+    _lib = lib
+    return lib
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def sum_of_squares(x) -> float:
+    x = _f32(x).ravel()
+    return float(load().ref_sum_of_squares(x, x.size))
+
+
+def scale(x) -> np.float32:
+    x = _f32(x).ravel()
+    return np.float32(load().ref_scale(x, x.size))
+
+
+def pack_signs(x) -> np.ndarray:
+    x = _f32(x).ravel()
+    words = np.zeros((x.size + 63) // 64, dtype=np.uint64)
+    load().ref_pack_signs(x, x.size, words)
+    return words
+
+
+def widen(g: np.ndarray) -> np.ndarray:
+    """fp32 gradients as they are; bf16 (uint16 bit patterns) widened exactly."""
+    if g.dtype == np.uint16:
+        return (g.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return _f32(g)
+
+
+def compression_step(p, m, v, err_s, err_w, grads, beta1: float, lr: float, eps: float) -> dict:
+    """One step of one tensor on copies of the state.  grads [W][n] (fp32 or
+    bf16 bit patterns).  Returns the new p, m, err_s, err_w and the messages:
+    packed_w [W][ceil(n/64)], scale_w [W], packed_s [ceil(n/64)], scale_s (fp32)."""
+    g = np.ascontiguousarray(widen(np.asarray(grads)))
+    W, n = g.shape
+    nw = (n + 63) // 64
+    out = {"p": _f32(p).copy(), "m": _f32(m).copy(), "err_s": _f32(err_s).copy(),
+           "err_w": _f32(err_w).reshape(W, n).copy(),
+           "packed_w": np.zeros((W, nw), dtype=np.uint64), "scale_w": np.zeros(W, dtype=np.float32),
+           "packed_s": np.zeros(nw, dtype=np.uint64), "scale_s": np.zeros(1, dtype=np.float32)}
+    st = load().ref_compression_step(n, W, g, float(beta1), float(lr), float(eps), out["p"], out["m"],
+                                     _f32(v), out["err_s"], out["err_w"], out["packed_w"],
+                                     out["scale_w"], out["packed_s"], out["scale_s"])
+    if st != 0:
+        raise ValueError("ref_compression_step rejected its arguments")
+    out["scale_s"] = out["scale_s"][0]
+    return out

@@ -1,0 +1,185 @@
+"""Pins of the C++ oracle (oracle/onebit_ref.cpp), CPU only.
+
+The C++ oracle is a second, independent implementation of the compression
+step.  It is pinned to things other than itself: math.fsum (the correctly
+rounded sum; an fp32 square is exact in fp64, so fsum of the squares is the
+exact sum rounded once), hand-made rounding ties, a pure-Python packer, the
+hand-derived worked example in tests/golden/, and, element by element and bit
+for bit, the numpy oracle (itself pinned by tests/pins.py) over ragged sizes,
+several worker counts, bf16 gradients, special values and chained steps.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.onebit as ob
+import oracle.ref as ref
+from golden_io import floats, ints, load
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _fsum_sq(x):
+    return math.fsum(float(v) * float(v) for v in np.asarray(x, dtype=np.float32).ravel())
+
+
+def _random_finite(rng, n):
+    """fp32 values with every exponent, subnormals included (random bit patterns)."""
+    u = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    return np.where(np.isfinite(x), x, np.float32(1.5)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "wide", "subnormal", "mixed"])
+def test_sum_of_squares_is_fsum(kind):
+    rng = _rng(11)
+    for n in (1, 2, 63, 1000, 20000):
+        if kind == "normal":
+            x = rng.normal(0.0, 1e-3, n).astype(np.float32)
+        elif kind == "wide":
+            x = _random_finite(rng, n)
+        elif kind == "subnormal":
+            x = (rng.integers(-(1 << 23), 1 << 23, n).astype(np.int64) * 2.0 ** -149).astype(np.float32)
+        else:
+            x = np.concatenate([rng.normal(0, 1e30, n // 2), rng.normal(0, 1e-30, n - n // 2)]).astype(np.float32)
+        assert ref.sum_of_squares(x) == _fsum_sq(x), (kind, n)
+        assert ref.sum_of_squares(x) == ob.sum_of_squares(x), (kind, n)
+
+
+def test_sum_of_squares_rounding_ties():
+    t = np.float32(2.0 ** -27)   # t^2 = 2^-54, a quarter of an ulp of 1
+    one = np.float32(1.0)
+    cases = {
+        (one, t): 1.0,                              # below half an ulp: down
+        (one, t, t): 1.0,                           # exactly half, even: stays
+        (one, t, t, t): 1.0 + 2.0 ** -52,           # above half: up
+        (np.float32(1.0 + 2.0 ** -23), t, t): None,  # a longer significand: checked against fsum only
+    }
+    for xs, want in cases.items():
+        x = np.array(xs, dtype=np.float32)
+        got = ref.sum_of_squares(x)
+        assert got == _fsum_sq(x), xs
+        if want is not None:
+            assert got == want, xs
+    # sticky bit: half an ulp plus a tiny remainder rounds up
+    x = np.array([1.0, 2.0 ** -27, 2.0 ** -27, 2.0 ** -60], dtype=np.float32)
+    assert ref.sum_of_squares(x) == 1.0 + 2.0 ** -52 == _fsum_sq(x)
+
+
+def test_scale_closed_forms_and_nonfinite():
+    for a in (0.75, 3.0, 2.0 ** -70, 2.0 ** 60, 1e-45):
+        for n in (1, 5, 64, 1001):
+            x = np.full(n, np.float32(a))
+            x[::3] = -x[::3]
+            assert ref.scale(x) == np.float32(a), (a, n)
+    assert ref.scale(np.zeros(10, np.float32)) == 0.0
+    for bad in (np.nan, np.inf, -np.inf):
+        x = np.ones(70, np.float32)
+        x[33] = bad
+        assert math.isnan(ref.sum_of_squares(x)) and np.isnan(ref.scale(x))
+    x = np.array([3.0, 4.0], np.float32)
+    assert ref.scale(x) == np.float32(math.sqrt(12.5))
+
+
+def test_pack_signs_brute_force():
+    rng = _rng(3)
+    x = np.array([0.0, -0.0, 1e-45, -1e-45, np.inf, -np.inf, np.nan, 1.0, -1.0], dtype=np.float32)
+    assert int(ref.pack_signs(x)[0]) == sum(1 << k for k, b in enumerate([1, 1, 1, 0, 1, 0, 0, 1, 0]) if b)
+    for n in (1, 63, 64, 65, 127, 129, 1000, 4097):
+        x = rng.normal(size=n).astype(np.float32)
+        want = [0] * ((n + 63) // 64)
+        for i in range(n):
+            if x[i] >= 0:
+                want[i // 64] |= 1 << (i % 64)
+        assert [int(w) for w in ref.pack_signs(x)] == want, n
+
+
+def test_golden_two_step():
+    g = load("worked_two_workers.txt")
+    beta1, lr, eps = (floats(g[k])[0] for k in ("beta1", "lr", "eps"))
+    f = lambda k: np.array(floats(g[k]), dtype=np.float32)  # noqa: E731
+    p, m, v = f("p0"), np.zeros(2, np.float32), f("v")
+    err_s, err_w = np.zeros(2, np.float32), np.zeros((2, 2), np.float32)
+    for step in ("step1", "step2"):
+        grads = np.stack([f(step + ".g0"), f(step + ".g1")])
+        out = ref.compression_step(p, m, v, err_s, err_w, grads, beta1, lr, eps)
+        for w in range(2):
+            assert [int(x) for x in out["packed_w"][w]] == ints(g[f"{step}.word{w}"]), (step, w)
+            assert float(out["scale_w"][w]) == floats(g[f"{step}.scale{w}"])[0], (step, w)
+            assert out["err_w"][w].tolist() == floats(g[f"{step}.err{w}"]), (step, w)
+        assert [int(x) for x in out["packed_s"]] == ints(g[step + ".server_word"]), step
+        assert float(out["scale_s"]) == floats(g[step + ".server_scale"])[0], step
+        assert out["err_s"].tolist() == floats(g[step + ".err_s"]), step
+        assert out["m"].tolist() == floats(g[step + ".m"]), step
+        assert out["p"].tolist() == floats(g[step + ".p"]), step
+        p, m, err_s, err_w = out["p"], out["m"], out["err_s"], out["err_w"]
+
+
+def _bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _same(a, b):
+    return np.array_equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("n,W,dtype", [(1, 1, "f32"), (63, 2, "f32"), (64, 3, "f32"), (65, 8, "f32"),
+                                       (1000, 9, "f32"), (8193, 4, "f32"), (777, 8, "bf16"),
+                                       (130, 64, "f32")])
+def test_step_equals_numpy_oracle(n, W, dtype):
+    """Three chained steps from the same state: every output bit-identical."""
+    rng = _rng(1000 + n + W)
+    beta1, lr, eps = 0.9, 1e-4, 1e-8
+    st = ob.TensorState(p=rng.normal(0, 0.02, n).astype(np.float32), m=np.zeros(n, np.float32),
+                        v=(np.abs(rng.normal(0, 1e-3, n)) ** 2 + 1e-12).astype(np.float32),
+                        err_s=np.zeros(n, np.float32), err_w=np.zeros((W, n), np.float32))
+    cst = {"p": st.p.copy(), "m": st.m.copy(), "err_s": st.err_s.copy(), "err_w": st.err_w.copy()}
+    for k in range(3):
+        g = rng.normal(0, 1e-3, (W, n)).astype(np.float32)
+        if k == 1:   # special values: zeros, negative zeros, subnormals
+            g[:, ::7] = 0.0
+            g[:, 3::11] = -0.0
+            g[:, 5::13] = np.float32(1e-42)
+        if dtype == "bf16":
+            g = (g.view(np.uint32) >> np.uint32(16)).astype(np.uint16)   # truncated bf16 patterns
+        out = ob.compression_step(st, g, beta1, lr, eps)
+        c = ref.compression_step(cst["p"], cst["m"], st.v, cst["err_s"], cst["err_w"], g, beta1, lr, eps)
+        words, scales = ob.words_of(out.worker_msgs)
+        assert _same(c["packed_w"], words) and _same(c["scale_w"], scales), k
+        assert _same(c["packed_s"], out.server_msg.words) and c["scale_s"] == out.server_msg.scale, k
+        for key, want in (("p", out.state.p), ("m", out.state.m), ("err_s", out.state.err_s),
+                          ("err_w", out.state.err_w)):
+            assert _same(c[key], want), (k, key)
+        st = out.state
+        cst = {key: c[key] for key in ("p", "m", "err_s", "err_w")}
+
+
+def test_step_nan_gradient_matches_numpy_oracle():
+    rng = _rng(5)
+    n, W = 200, 3
+    st = ob.TensorState(p=rng.normal(0, 0.02, n).astype(np.float32), m=np.zeros(n, np.float32),
+                        v=np.full(n, 1e-6, np.float32), err_s=np.zeros(n, np.float32),
+                        err_w=np.zeros((W, n), np.float32))
+    g = rng.normal(0, 1e-3, (W, n)).astype(np.float32)
+    g[1, 17] = np.nan
+    out = ob.compression_step(st, g, 0.9, 1e-4, 1e-8)
+    c = ref.compression_step(st.p, st.m, st.v, st.err_s, st.err_w, g, 0.9, 1e-4, 1e-8)
+    assert np.isnan(c["scale_w"][1]) and not np.isnan(c["scale_w"][0])
+    words, scales = ob.words_of(out.worker_msgs)
+    assert _same(c["packed_w"], words)
+    np.testing.assert_array_equal(c["scale_w"], scales)
+    for key, want in (("p", out.state.p), ("m", out.state.m), ("err_s", out.state.err_s),
+                      ("err_w", out.state.err_w)):
+        np.testing.assert_array_equal(c[key], want, err_msg=key)
+
+
+def test_rejects_bad_arguments():
+    lib = ref.load()
+    one = np.zeros(1, np.float32)
+    w = np.zeros(1, np.uint64)
+    assert lib.ref_compression_step(0, 1, one, 0.9, 1e-4, 1e-8, one, one, one, one, one, w, one, w, one) == 1
+    assert lib.ref_compression_step(1, 0, one, 0.9, 1e-4, 1e-8, one, one, one, one, one, w, one, w, one) == 1
