@@ -455,7 +455,7 @@ def main() -> int:
     ap.add_argument("--cltk-density", type=float, default=0.01,
                     help="also time the cyclic local top-k exchange keeping this fraction of "
                          "each tensor (0 = skip)")
-    ap.add_argument("--cpu-sample-tensors", type=int, default=128)
+    ap.add_argument("--cpu-sample-tensors", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/<workload>_hbm_counters.json from rocprofv3 --pmc runs "
