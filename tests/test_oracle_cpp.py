@@ -183,3 +183,26 @@ def test_rejects_bad_arguments():
     w = np.zeros(1, np.uint64)
     assert lib.ref_compression_step(0, 1, one, 0.9, 1e-4, 1e-8, one, one, one, one, one, w, one, w, one) == 1
     assert lib.ref_compression_step(1, 0, one, 0.9, 1e-4, 1e-8, one, one, one, one, one, w, one, w, one) == 1
+
+
+def test_single_tensor_workload_trajectory_equals_numpy_oracle():
+    """The single-tensor workload (n = 2^20, W = 4, 10 steps, its seeded inputs
+    generated on the CPU): the two oracles agree bit for bit after every step."""
+    from synth import WORKLOADS, grads_for_step, host_slice, init_state
+    wl = WORKLOADS["single_tensor_2p20"]
+    n = wl.numel[0]
+    st0 = init_state(wl, "cpu")
+    st = ob.TensorState(*(host_slice(st0[k], 0, n) for k in ("p", "m", "v", "err_s", "err_w")))
+    cst = {k: getattr(st, k).copy() for k in ("p", "m", "err_s", "err_w")}
+    for k in range(wl.steps):
+        g = host_slice(grads_for_step(wl, k, "cpu"), 0, n)
+        out = ob.compression_step(st, g, wl.beta1, wl.lr, wl.eps)
+        c = ref.compression_step(cst["p"], cst["m"], st.v, cst["err_s"], cst["err_w"], g, wl.beta1, wl.lr,
+                                 wl.eps)
+        words, scales = ob.words_of(out.worker_msgs)
+        assert _same(c["packed_w"], words) and _same(c["scale_w"], scales), k
+        assert _same(c["packed_s"], out.server_msg.words) and c["scale_s"] == out.server_msg.scale, k
+        for key in ("p", "m", "err_s", "err_w"):
+            assert _same(c[key], getattr(out.state, key)), (k, key)
+        st = out.state
+        cst = {key: c[key] for key in ("p", "m", "err_s", "err_w")}
