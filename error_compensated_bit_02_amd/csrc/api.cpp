@@ -32,6 +32,8 @@ struct ob_ctx {
   std::vector<int64_t> off;
   int64_t N = 0;
   int32_t num_tiles = 0;
+  int32_t max_tensor_tiles = 0;      // tiles of the largest tensor
+  int32_t max_piece_tiles = 0;       // tiles of the largest server piece
   std::vector<int32_t> tile_begin;   // host copy [T+1]
   int32_t server_chunks = 1;
   int32_t S = 0;                     // server scales (pieces)
@@ -161,7 +163,7 @@ int do_compress(ob_ctx *c, int w0, int w1, const void *grads, const float *m, fl
   if (st) return st;
   st = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
     ob::launch_scale_finalize(g, c->partials, g.num_tiles, 1, w0, w1 - w0, g.tile_begin, g.numel, c->T,
-                              scale_w + static_cast<size_t>(w0) * c->T, s);
+                              scale_w + static_cast<size_t>(w0) * c->T, c->max_tensor_tiles, s);
   });
   if (st) return st;
   return timed(c, ob::K_WORKER_PASS2, s, [&] {
@@ -179,7 +181,7 @@ int do_server_first(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, f
   if (st) return st;
   return timed(c, ob::K_SCALE_FINALIZE, s, [&] {
     ob::launch_scale_finalize(g, c->partials, g.num_tiles, 1, c->W, 1, g.piece_begin, g.piece_numel, c->S,
-                              scale_s, s);
+                              scale_s, c->max_piece_tiles, s);
   });
 }
 
@@ -206,6 +208,7 @@ int do_update(ob_ctx *c, bool store_m, ob::Kind kind, const uint64_t *packed_s,
 int upload_pieces(ob_ctx *c, int32_t chunks) {
   std::vector<int32_t> tile_piece(c->num_tiles), piece_begin;
   std::vector<int64_t> piece_numel;
+  int32_t max_piece = 0;
   for (int32_t t = 0; t < c->T; ++t) {
     const int32_t k = c->tile_begin[t + 1] - c->tile_begin[t];
     const int32_t q = (k + chunks - 1) / chunks;
@@ -215,6 +218,7 @@ int upload_pieces(ob_ctx *c, int32_t chunks) {
       const int64_t lo = static_cast<int64_t>(i) * ob::kTile;
       const int64_t hi = std::min<int64_t>(static_cast<int64_t>(i + q) * ob::kTile, c->numel[t]);
       piece_numel.push_back(hi - lo);
+      max_piece = std::max(max_piece, std::min(i + q, k) - i);
       for (int32_t j = i; j < std::min(i + q, k); ++j) tile_piece[c->tile_begin[t] + j] = piece;
     }
   }
@@ -228,6 +232,7 @@ int upload_pieces(ob_ctx *c, int32_t chunks) {
                 hipMemcpyHostToDevice) != hipSuccess)
     return OB_ERR_DEVICE;
   c->server_chunks = chunks;
+  c->max_piece_tiles = max_piece;
   c->S = static_cast<int32_t>(S);
   c->geo.S = c->S;
   return OB_OK;
@@ -289,7 +294,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   // The largest launches must fit the device's grid limit: (worker group,
   // tile) workgroups of the strict worker passes, (chunk, worker) workgroups
   // of the residual one (chunks along x, workers along y), and the scale
-  // finalize's one wavefront per (worker, tensor).
+  // finalize's up to one workgroup per (worker, tensor).
   int64_t nt = 0;
   for (int32_t t = 0; t < num_tensors; ++t) nt += (numel[t] + ob::kTile - 1) / ob::kTile;
   if (nt * ob::kChunksPerTile > ob::kMaxGrid) {
@@ -297,7 +302,7 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
     return OB_ERR_INVALID;
   }
   const int64_t wgroup = ob::worker_group_size(num_workers, static_cast<int>(nt));
-  const int64_t finalize = (static_cast<int64_t>(num_workers) * num_tensors + ob::kWaves - 1) / ob::kWaves;
+  const int64_t finalize = static_cast<int64_t>(num_workers) * num_tensors;
   if (nt * ((num_workers + wgroup - 1) / wgroup) > ob::kMaxGrid || finalize > ob::kMaxGrid) {
     delete c;
     return OB_ERR_INVALID;
@@ -316,6 +321,8 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   tile_begin[num_tensors] = static_cast<int32_t>(tiles.size());
   c->num_tiles = static_cast<int32_t>(tiles.size());
   c->tile_begin = tile_begin;
+  for (int32_t t = 0; t < num_tensors; ++t)
+    c->max_tensor_tiles = std::max(c->max_tensor_tiles, tile_begin[t + 1] - tile_begin[t]);
 
   // one allocation, 256-byte aligned sections
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
@@ -475,7 +482,8 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   if (r) return r;
   r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
     ob::launch_scale_finalize(g, c->chunk_partials, static_cast<int64_t>(g.num_tiles) * ob::kChunksPerTile,
-                              ob::kChunksPerTile, 0, c->W, g.tile_begin, g.numel, c->T, scale_w, s);
+                              ob::kChunksPerTile, 0, c->W, g.tile_begin, g.numel, c->T, scale_w,
+                              static_cast<int64_t>(c->max_tensor_tiles) * ob::kChunksPerTile, s);
   });
   if (r) return r;
   const ob::ServerArgs sa = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
@@ -485,7 +493,7 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   if (r) return r;
   r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
     ob::launch_scale_finalize(g, c->partials, g.num_tiles, 1, c->W, 1, g.piece_begin, g.piece_numel, c->S,
-                              scale_s, s);
+                              scale_s, c->max_piece_tiles, s);
   });
   if (r) return r;
   return do_update(c, false, ob::K_UPDATE_RESIDUAL, packed_s, scale_s, v, nullptr, params, lr, s);

@@ -206,9 +206,14 @@ void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerAr
 // `per` pairs per tile) over `count` items whose tile ranges are begin[i] ..
 // begin[i+1]-1 and sizes numel[i]; row r's scale of item i goes to
 // out[(r - row0) * count + i].
+// Scales from partial sums: items [row0, row0 + nrows) x [0, count), item i
+// of a row summing partials [begin[i] * per, begin[i + 1] * per).  A whole
+// workgroup per item when the largest item has at least kWideFinalize
+// partials, one wavefront per item otherwise.
+constexpr int64_t kWideFinalize = 4096;
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int64_t cols, int per, int row0,
                            int nrows, const int32_t *begin, const int64_t *numel, int count, float *out,
-                           hipStream_t s);
+                           int64_t max_item_partials, hipStream_t s);
 void launch_server(ServerPass pass, const Geometry &g, const ServerArgs &a, hipStream_t s);
 // with_ratio: p -= lr * (ratio[t] * u), u = m / (sqrt(v) + eps) (+ wd * p)
 void launch_update(bool store_m, bool with_ratio, const Geometry &g, const UpdateArgs &a,

@@ -360,32 +360,43 @@ __global__ __launch_bounds__(kBlock) void worker_chunk_kernel(Geometry g, Worker
 }
 
 // ---------------------------------------------------------------------------
-// scale finalize: one wavefront per (row, tensor)
+// scale finalize: kItemWaves wavefronts per (row, tensor) item
+//
+// One wavefront per item when every item is small; a whole workgroup per item
+// when some item has many partials (a 31 M-element embedding has 30,520
+// per-chunk partials per worker, which one wavefront reads 8 KB at a time).
 // ---------------------------------------------------------------------------
+template <int kItemWaves>
 __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
                                                          const double2 *__restrict__ partials,
                                                          int64_t cols, int per, int row0, int nrows,
                                                          const int32_t *__restrict__ begin,
                                                          const int64_t *__restrict__ numel,
                                                          int count, float *__restrict__ out) {
+  static_assert(kItemWaves == 1 || kItemWaves == kWaves, "a wavefront or a workgroup per item");
+  __shared__ double2 red[kWaves];
   const int lane = threadIdx.x & 63;
-  const int64_t id = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (id >= static_cast<int64_t>(nrows) * count) return;  // whole wavefront leaves together
+  const int wave = threadIdx.x >> 6;
+  const int sub = wave % kItemWaves;   // this wavefront's share of its item
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * (kWaves / kItemWaves) + wave / kItemWaves;
+  if (id >= static_cast<int64_t>(nrows) * count) return;  // the item's wavefronts leave together
   const int r = static_cast<int>(id / count);
   const int item = static_cast<int>(id % count);
   const double2 *row = partials + static_cast<size_t>(row0 + r) * cols;
-  // eight independent chains per lane, their loads issued together, then
-  // folded in a fixed order
+  // eight independent chains per thread, their loads issued together, then
+  // folded in a fixed order: per thread, per wavefront, across the wavefronts
   constexpr int kChains = 8;
+  constexpr int kThreads = 64 * kItemWaves;
   double ch[kChains], cl[kChains];
 #pragma unroll
   for (int k = 0; k < kChains; ++k) ch[k] = cl[k] = 0.0;
   const int64_t end = static_cast<int64_t>(begin[item + 1]) * per;
-  for (int64_t i0 = static_cast<int64_t>(begin[item]) * per + lane; i0 < end; i0 += 64 * kChains) {
+  for (int64_t i0 = static_cast<int64_t>(begin[item]) * per + 64 * sub + lane; i0 < end;
+       i0 += kThreads * kChains) {
     double2 p[kChains];
 #pragma unroll
     for (int k = 0; k < kChains; ++k) {
-      const int64_t i = i0 + 64 * k;
+      const int64_t i = i0 + kThreads * k;
       p[k] = i < end ? row[i] : make_double2(0.0, 0.0);
     }
 #pragma unroll
@@ -400,11 +411,20 @@ __global__ __launch_bounds__(kBlock) void scale_finalize(Geometry g,
     const double ol = __shfl_xor(lo, d);
     dd_add(hi, lo, oh, ol);
   }
-  if (lane == 0) {
-    const double S = hi + lo;                          // fl64 of the sum of squares
-    const double q = S / static_cast<double>(numel[item]);
-    out[static_cast<size_t>(r) * count + item] = static_cast<float>(__builtin_sqrt(q));
+  if (kItemWaves > 1) {   // the whole workgroup is one item: fold the wavefronts in order
+    if (lane == 0) red[sub] = make_double2(hi, lo);
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    hi = red[0].x;
+    lo = red[0].y;
+#pragma unroll
+    for (int v = 1; v < kItemWaves; ++v) dd_add(hi, lo, red[v].x, red[v].y);
+  } else if (lane != 0) {
+    return;
   }
+  const double S = hi + lo;                          // fl64 of the sum of squares
+  const double q = S / static_cast<double>(numel[item]);
+  out[static_cast<size_t>(r) * count + item] = static_cast<float>(__builtin_sqrt(q));
 }
 
 // ---------------------------------------------------------------------------
@@ -823,11 +843,16 @@ void launch_worker(WorkerPass pass, const Geometry &g, bool bf16, const WorkerAr
 
 void launch_scale_finalize(const Geometry &g, const double2 *partials, int64_t cols, int per, int row0,
                            int nrows, const int32_t *begin, const int64_t *numel, int count, float *out,
-                           hipStream_t s) {
-  const int64_t waves = static_cast<int64_t>(nrows) * count;
-  const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves)), block(kBlock);
-  hipLaunchKernelGGL(scale_finalize, grid, block, 0, s, g, partials, cols, per, row0, nrows, begin,
-                     numel, count, out);
+                           int64_t max_item_partials, hipStream_t s) {
+  const int64_t items = static_cast<int64_t>(nrows) * count;
+  const dim3 block(kBlock);
+  if (max_item_partials >= kWideFinalize) {
+    hipLaunchKernelGGL((scale_finalize<kWaves>), dim3(static_cast<unsigned>(items)), block, 0, s, g, partials,
+                       cols, per, row0, nrows, begin, numel, count, out);
+  } else {
+    hipLaunchKernelGGL((scale_finalize<1>), dim3(static_cast<unsigned>((items + kWaves - 1) / kWaves)), block,
+                       0, s, g, partials, cols, per, row0, nrows, begin, numel, count, out);
+  }
 }
 
 template <bool kPow2>

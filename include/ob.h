@@ -102,7 +102,7 @@ int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off);
  * with synchronous copies.  OB_ERR_INVALID also when a launch over the list
  * would exceed the device's grid limit (2^32 - 1 work-items, i.e. 16,777,215
  * workgroups of 256): the (worker group, tile) grid of 8192-element tiles,
- * the 1024-element chunks of the residual worker pass, or one wavefront per
+ * the 1024-element chunks of the residual worker pass, or one workgroup per
  * (worker, tensor) for the scales.  OB_ERR_NOMEM when the
  * scratch cannot be allocated.  Blocking calls of this library: ob_init,
  * ob_destroy, ob_set_server_chunks, ob_cltk_configure and ob_profile_read;

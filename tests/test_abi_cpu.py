@@ -88,8 +88,8 @@ def test_init_rejects_lists_beyond_the_grid_limit(lib):
     """Checked on the host before any device call: 2^40 elements is 2^27 tiles
     of 8192, beyond 16,777,215 workgroups; 2^34 elements is 2^21 tiles, whose
     2^24 chunks of 1024 (the residual worker pass) exceed it by one; 4096
-    workers x 20,000 tensors needs 81.92 M scale wavefronts, 20.48 M
-    workgroups of 4."""
+    workers x 20,000 tensors needs up to 81.92 M scale workgroups (one per
+    worker and tensor)."""
     ctx = ctypes.c_void_p()
     big = (ctypes.c_int64 * 1)(1 << 40)
     assert lib.ob_init(ctypes.byref(ctx), 1, big, 1, 0, 0.9, 1e-8) == 1
