@@ -662,8 +662,23 @@ __global__ __launch_bounds__(kBlock) void trust_ratio_kernel(Geometry g,
 #pragma unroll
   for (int row = 0; row < 2; ++row) {
     const double2 *p = partials + static_cast<size_t>(row) * g.num_tiles;
-    double hi = 0.0, lo = 0.0;
-    for (int i = g.tile_begin[t] + lane; i < g.tile_begin[t + 1]; i += 64) dd_add(hi, lo, p[i].x, p[i].y);
+    // eight independent chains per lane, their loads issued together, then
+    // folded in a fixed order
+    constexpr int kChains = 8;
+    double ch[kChains], cl[kChains];
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) ch[k] = cl[k] = 0.0;
+    const int end = g.tile_begin[t + 1];
+    for (int i0 = g.tile_begin[t] + lane; i0 < end; i0 += 64 * kChains) {
+      double2 q[kChains];
+#pragma unroll
+      for (int k = 0; k < kChains; ++k) q[k] = i0 + 64 * k < end ? p[i0 + 64 * k] : make_double2(0.0, 0.0);
+#pragma unroll
+      for (int k = 0; k < kChains; ++k) dd_add(ch[k], cl[k], q[k].x, q[k].y);
+    }
+    double hi = ch[0], lo = cl[0];
+#pragma unroll
+    for (int k = 1; k < kChains; ++k) dd_add(hi, lo, ch[k], cl[k]);
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       const double oh = __shfl_xor(hi, d);
