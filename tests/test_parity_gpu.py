@@ -116,6 +116,33 @@ def test_worker_subranges():
     assert torch.equal(a.bufs["scale_w"], b.bufs["scale_w"])
 
 
+def test_worker_subranges_large_tensor_against_oracle():
+    """A tensor of 4097 tiles (its scales take the finalize with a workgroup per
+    (worker, tensor)) beside a small one: workers [1, 3) then [0, 1) through
+    ob_compress_worker equal all three at once, and the scales and signs of a
+    sampled worker equal the oracle's."""
+    n_big = 4097 * 8192 - 5
+    wl = _wl("subrange_big_w3", (n_big, 777), 3, steps=1)
+    a, b = Run(wl), Run(wl)
+    g = grads_for_step(wl, 0, "cuda")
+    a.ctx.compress_worker(g, a.state["m"], a.state["err_w"], a.bufs["packed_w"], a.bufs["scale_w"])
+    b.ctx.compress_worker(g, b.state["m"], b.state["err_w"], b.bufs["packed_w"], b.bufs["scale_w"], 1, 3)
+    b.ctx.compress_worker(g, b.state["m"], b.state["err_w"], b.bufs["packed_w"], b.bufs["scale_w"], 0, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.state["err_w"], b.state["err_w"])
+    assert torch.equal(a.bufs["packed_w"], b.bufs["packed_w"])
+    assert torch.equal(a.bufs["scale_w"], b.bufs["scale_w"])
+    off = a.off
+    for t, n in enumerate(wl.numel):
+        # worker 2 from the initial state: m = 0 (read only here) and e = 0
+        m = host_slice(a.state["m"], off[t], off[t] + n)
+        x = ob.worker_momentum(m, host_slice(g, off[t], off[t] + n)[2], wl.beta1) + np.zeros(n, np.float32)
+        msg = ob.OneBitCompressor.compress(x)
+        got_w = a.bufs["packed_w"][2, off[t] // 64: off[t] // 64 + (n + 63) // 64].cpu().numpy().view(np.uint64)
+        assert np.array_equal(got_w, msg.words), t
+        assert a.bufs["scale_w"][2, t].item() == float(msg.scale), t
+
+
 def test_special_values_zero_nan_subnormal():
     """A zero tensor (scale 0, all bits 1), a tensor with -0/+0 and a NaN
     (scale NaN), and a tensor of subnormal gradients, against the oracle."""
