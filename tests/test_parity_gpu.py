@@ -143,11 +143,13 @@ def test_worker_subranges_large_tensor_against_oracle():
         assert a.bufs["scale_w"][2, t].item() == float(msg.scale), t
 
 
-def test_special_values_zero_nan_subnormal():
+@pytest.mark.parametrize("residual", [False, True], ids=["strict", "residual"])
+def test_special_values_zero_nan_subnormal(residual):
     """A zero tensor (scale 0, all bits 1), a tensor with -0/+0 and a NaN
-    (scale NaN), and a tensor of subnormal gradients, against the oracle."""
+    (scale NaN), and a tensor of subnormal gradients, against the oracle, in
+    both state forms."""
     sizes = (130, 70, 200)
-    wl = _wl("special_w2", sizes, 2, steps=2)
+    wl = _wl("special_w2", sizes, 2, steps=3)
     run_state = init_state(wl, "cuda")
     off, _ = padded_layout(wl.numel)
 
@@ -158,7 +160,7 @@ def test_special_values_zero_nan_subnormal():
         g[0, off[1] + 5] = float("nan")
         g[:, off[2]:off[2] + 200] *= 1e-38 / 1e-3     # subnormal and tiny normals
         return g
-    rep = parity_run(wl, wl.steps, grads_fn=grads_fn, state=run_state)
+    rep = parity_run(wl, wl.steps, grads_fn=grads_fn, state=run_state, residual=residual)
     _report(wl.name, rep)
 
 
