@@ -1,21 +1,25 @@
-"""Every element of a full-size tensor list against the C++ oracle.
+"""Every element of full-size tensor lists against the C++ oracle.
 
 The benchmark's launch configuration (the residual-form step over the whole
-list, one launch per kernel) on the BERT-Large-shaped list with 8 workers and
-the ResNet-50-shaped list with 32 workers; after every step, each tensor's
-sign words, scales, materialized errors, momentum and parameters are compared
-with the C++ oracle's step on the same inputs (copied to the host before the
-step).  The C++ oracle (oracle/onebit_ref.cpp) is pinned on the CPU by
-tests/test_oracle_cpp.py.
+list, one launch per kernel) on the BERT-Large-shaped list (W = 8), the
+ResNet-50-shaped list (W = 32), the BERT-base-shaped list (W = 64) and the
+GPT-1.3B-shaped list with bf16 gradients (W = 8).  After every step each
+tensor's sign words, scales, materialized errors, momentum and parameters are
+compared bit for bit with the C++ oracle's step, which runs on host copies of
+the same inputs and carries its own state from step to step.  The oracle runs
+one tensor per call from a pool of host threads.  The C++ oracle
+(oracle/onebit_ref.cpp) is pinned on the CPU by tests/test_oracle_cpp.py.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
 
-import oracle.onebit as ob
 import oracle.ref as ref
-from harness import Report, Run, log
-from synth import WORKLOADS, grads_for_step, host_slice
+from harness import Run, log
+from synth import WORKLOADS, grads_for_step
 
 pytestmark = pytest.mark.gpu
 
@@ -26,36 +30,74 @@ def _need_gpu():
         pytest.skip("no GPU visible")
 
 
-def _as_step_output(c: dict, v: np.ndarray, n: int) -> ob.StepOutput:
-    W = c["packed_w"].shape[0]
-    msgs = [ob.OneBitMessage(c["packed_w"][w], np.float32(c["scale_w"][w]), n) for w in range(W)]
-    state = ob.TensorState(c["p"], c["m"], v, c["err_s"], c["err_w"])
-    return ob.StepOutput(state, msgs, ob.OneBitMessage(c["packed_s"], np.float32(c["scale_s"]), n))
+def _host(t: torch.Tensor) -> np.ndarray:
+    """A whole device buffer on the host; bf16 as its uint16 patterns, int64 words as uint64."""
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    a = t.contiguous().cpu().numpy()
+    return a.view(np.uint64) if a.dtype == np.int64 else a
 
 
-@pytest.mark.parametrize("name,steps", [("resnet50_w32", 3), ("bert_large", 2)])
+def _same(a, b) -> bool:
+    a, b = np.asarray(a), np.asarray(b)
+    if a.dtype == np.float32:
+        a, b = a.view(np.uint32), np.asarray(b, np.float32).view(np.uint32)
+    return a.shape == b.shape and np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name,steps", [("resnet50_w32", 3), ("bert_large", 2), ("bert_base_w64", 1),
+                                        ("gpt_1p3b_bf16", 1)])
 def test_every_element_against_cpp_oracle(name, steps):
     wl = WORKLOADS[name]
-    log(f"{name}: {steps} residual-form steps, every tensor against the C++ oracle")
+    threads = max(1, min(16, os.cpu_count() or 1))
+    log(f"{name}: {steps} residual-form steps, every tensor against the C++ oracle ({threads} threads)")
     ref.load()
     run = Run(wl)
-    host = run.host_state(range(wl.num_tensors))
-    rep = Report()
+    off, W = run.off, wl.workers
+    host = {k: _host(run.state[k]) for k in ("p", "m", "v", "err_s", "err_w")}
+    # the oracle's own state, per tensor
+    states = []
+    for t, n in enumerate(wl.numel):
+        lo, hi = off[t], off[t] + n
+        states.append({k: np.ascontiguousarray(host[k][..., lo:hi]) for k in host})
+    del host
     gbuf = None
+    words = floats = 0
     for k in range(steps):
         gbuf = grads_for_step(wl, k, "cuda", out=gbuf)
+        g = _host(gbuf)
         run.step_residual(gbuf, first=(k == 0))
         view = run.materialized()
         torch.cuda.synchronize()
-        for t in range(wl.num_tensors):
-            lo, hi = run.off[t], run.off[t] + wl.numel[t]
-            st = host[t]
-            c = ref.compression_step(st.p, st.m, st.v, st.err_s, st.err_w, host_slice(gbuf, lo, hi),
-                                     wl.beta1, wl.lr, wl.eps)
-            out = _as_step_output(c, st.v, wl.numel[t])
-            run.compare(t, out, rep, f"{name} step {k} {wl.tensors[t][0]}", state=view)
-            host[t] = out.state
+        got = {"p": _host(run.state["p"]), "m": _host(view["m"]), "err_s": _host(view["err_s"]),
+               "err_w": _host(view["err_w"]), "packed_w": _host(run.bufs["packed_w"]),
+               "scale_w": _host(run.bufs["scale_w"]), "packed_s": _host(run.bufs["packed_s"]),
+               "scale_s": _host(run.bufs["scale_s"])}
         del view
-        log(f"{name} step {k}: {rep.words} sign words and {rep.total_floats} floats compared, "
-            f"{rep.exact_floats} floats bit-identical")
-    assert rep.exact_floats == rep.total_floats
+
+        def check(t):
+            n = wl.numel[t]
+            lo, hi = off[t], off[t] + n
+            wlo, whi = lo // 64, lo // 64 + (n + 63) // 64
+            st = states[t]
+            c = ref.compression_step(st["p"], st["m"], st["v"], st["err_s"], st["err_w"],
+                                     np.ascontiguousarray(g[:, lo:hi]), wl.beta1, wl.lr, wl.eps)
+            bad = [key for key, mine, dev in (
+                ("packed_w", c["packed_w"], got["packed_w"][:, wlo:whi]),
+                ("scale_w", c["scale_w"], got["scale_w"][:, t]),
+                ("packed_s", c["packed_s"], got["packed_s"][wlo:whi]),
+                ("scale_s", np.float32(c["scale_s"]), got["scale_s"][t]),
+                ("p", c["p"], got["p"][lo:hi]), ("m", c["m"], got["m"][lo:hi]),
+                ("err_s", c["err_s"], got["err_s"][lo:hi]), ("err_w", c["err_w"], got["err_w"][:, lo:hi]),
+            ) if not _same(mine, dev)]
+            states[t] = {"p": c["p"], "m": c["m"], "v": st["v"], "err_s": c["err_s"], "err_w": c["err_w"]}
+            return t, bad, W * ((n + 63) // 64) + (n + 63) // 64, (3 + W) * n + W + 1
+
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            results = list(pool.map(check, sorted(range(wl.num_tensors), key=lambda t: -wl.numel[t])))
+        failed = [(wl.tensors[t][0], bad) for t, bad, _, _ in results if bad]
+        words += sum(r[2] for r in results)
+        floats += sum(r[3] for r in results)
+        assert not failed, f"{name} step {k}: {len(failed)} tensors differ, first {failed[:3]}"
+        log(f"{name} step {k}: {words} sign words and {floats} floats compared, all bit-identical")
+        del got, g
