@@ -1,5 +1,5 @@
 // Plain, single-threaded C++ oracle of one compression-phase step of 1-bit
-// Adam, for one tensor.
+// Adam, and of one warmup-phase (uncompressed Adam) step, for one tensor.
 //
 // TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the
 // build entry module and the CPU-baseline leg of the benchmark load this
@@ -28,6 +28,8 @@
 //   momentum after the step: the server's reconstruction               (R7)
 //   update    p - lr*(m/(sqrt(v)+eps)), fp32, correctly rounded       (R8)
 //   a NaN or Inf anywhere in a tensor makes its scale NaN              (R9)
+//   warmup    Adam on the R6 average of the gradients, v with
+//             b2 = fp32(beta2), cb2 = fp32(1 - beta2), no bias correction (R10)
 // Every fp32 product and sum below is its own statement and the file is
 // compiled with -ffp-contract=off, so each rounds once.
 
@@ -211,6 +213,43 @@ int ref_compression_step(int64_t n, int32_t W, const float *g, double beta1, dou
     m[i] = mhat;
     const float d = std::sqrt(v[i]) + eps32;
     const float u = mhat / d;
+    const float step = lr32 * u;
+    p[i] = p[i] - step;
+  }
+  return 0;
+}
+
+// One warmup-phase step of one tensor: full-precision Adam on the workers'
+// average gradient (the review's Proposed method, bullet 1: Adam for about the
+// first 20% of steps), no bias correction (R10):
+//   gbar = (ascending fp32 sum over w of g_w, from +0) / W
+//   m = c1*m + c2*gbar;  v = b2*v + cb2*(gbar*gbar);  p = p - lr*(m/(sqrt(v)+eps))
+// with c1, c2 as in R5 and b2 = fp32(beta2), cb2 = fp32(1 - beta2) (complement
+// in double).  g [W][n] fp32; p, m, v [n] read and overwritten.  Returns 0, or
+// 1 for a bad argument.
+int ref_warmup_step(int64_t n, int32_t W, const float *g, double beta1, double beta2, double lr, double eps,
+                    float *p, float *m, float *v) {
+  if (n < 1 || W < 1 || !g || !p || !m || !v) return 1;
+  const float c1 = static_cast<float>(beta1);
+  const float c2 = static_cast<float>(1.0 - beta1);
+  const float b2 = static_cast<float>(beta2);
+  const float cb2 = static_cast<float>(1.0 - beta2);
+  const float wf = static_cast<float>(W);
+  const float lr32 = static_cast<float>(lr);
+  const float eps32 = static_cast<float>(eps);
+  for (int64_t i = 0; i < n; ++i) {
+    float acc = 0.0f;
+    for (int32_t w = 0; w < W; ++w) acc = acc + g[static_cast<size_t>(w) * n + i];
+    const float gbar = acc / wf;
+    const float m1 = c1 * m[i];
+    const float m2 = c2 * gbar;
+    m[i] = m1 + m2;
+    const float v1 = b2 * v[i];
+    const float sq = gbar * gbar;
+    const float v2 = cb2 * sq;
+    v[i] = v1 + v2;
+    const float d = std::sqrt(v[i]) + eps32;
+    const float u = m[i] / d;
     const float step = lr32 * u;
     p[i] = p[i] - step;
   }

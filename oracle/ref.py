@@ -1,5 +1,5 @@
 """ctypes front of the C++ oracle (oracle/onebit_ref.cpp): one compression-phase
-step of one tensor, plain and single-threaded.
+step and one warmup step of one tensor, plain and single-threaded.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the build
 entry module and the CPU-baseline leg of the benchmark may import this module.
@@ -64,6 +64,9 @@ def load() -> ctypes.CDLL:
     lib.ref_compression_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double,
                                          ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p, _f32p,
                                          _f32p, _u64p, _f32p, _u64p, _f32p]
+    lib.ref_warmup_step.restype = ctypes.c_int
+    lib.ref_warmup_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double, ctypes.c_double,
+                                    ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p]
     _lib = lib
     return lib
 
@@ -113,4 +116,17 @@ def compression_step(p, m, v, err_s, err_w, grads, beta1: float, lr: float, eps:
     if st != 0:
         raise ValueError("ref_compression_step rejected its arguments")
     out["scale_s"] = out["scale_s"][0]
+    return out
+
+
+def warmup_step(p, m, v, grads, beta1: float, beta2: float, lr: float, eps: float) -> dict:
+    """One warmup (uncompressed Adam) step of one tensor on copies of p, m, v;
+    grads [W][n] fp32 or bf16 bit patterns.  Returns the new p, m, v."""
+    g = np.ascontiguousarray(widen(np.asarray(grads)))
+    W, n = g.shape
+    out = {"p": _f32(p).copy(), "m": _f32(m).copy(), "v": _f32(v).copy()}
+    st = load().ref_warmup_step(n, W, g, float(beta1), float(beta2), float(lr), float(eps),
+                                out["p"], out["m"], out["v"])
+    if st != 0:
+        raise ValueError("ref_warmup_step rejected its arguments")
     return out

@@ -6,8 +6,9 @@ ResNet-50-shaped list (W = 32), the BERT-base-shaped list (W = 64) and the
 GPT-1.3B-shaped list with bf16 gradients (W = 8).  After every step each
 tensor's sign words, scales, materialized errors, momentum and parameters are
 compared bit for bit with the C++ oracle's step, which runs on host copies of
-the same inputs and carries its own state from step to step.  The oracle runs
-one tensor per call from a pool of host threads.  The C++ oracle
+the same inputs and carries its own state from step to step.  The warmup step
+(uncompressed Adam) likewise on the BERT-Large and GPT-1.3B lists.  The oracle
+runs one tensor per call from a pool of host threads.  The C++ oracle
 (oracle/onebit_ref.cpp) is pinned on the CPU by tests/test_oracle_cpp.py.
 """
 import os
@@ -100,4 +101,48 @@ def test_every_element_against_cpp_oracle(name, steps):
         floats += sum(r[3] for r in results)
         assert not failed, f"{name} step {k}: {len(failed)} tensors differ, first {failed[:3]}"
         log(f"{name} step {k}: {words} sign words and {floats} floats compared, all bit-identical")
+        del got, g
+
+
+@pytest.mark.parametrize("name,steps", [("bert_large", 2), ("gpt_1p3b_bf16", 1)])
+def test_warmup_every_element_against_cpp_oracle(name, steps):
+    """The warmup step (uncompressed Adam on the average gradient, from zero
+    moments) over the whole list, every element of p, m and v bit for bit."""
+    beta2, lr = 0.999, 1e-3
+    wl = WORKLOADS[name]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    log(f"{name}: {steps} warmup steps, every tensor against the C++ oracle ({threads} threads)")
+    ref.load()
+    run = Run(wl)
+    run.state["m"].zero_()
+    run.state["v"].zero_()
+    off = run.off
+    host = {k: _host(run.state[k]) for k in ("p", "m", "v")}
+    states = [{k: np.ascontiguousarray(host[k][off[t]:off[t] + n]) for k in host} for t, n in enumerate(wl.numel)]
+    del host
+    gbuf = None
+    floats = 0
+    for k in range(steps):
+        gbuf = grads_for_step(wl, k, "cuda", out=gbuf)
+        g = _host(gbuf)
+        run.ctx.warmup_step(gbuf, run.state["m"], run.state["v"], run.state["p"], beta2, lr)
+        torch.cuda.synchronize()
+        got = {key: _host(run.state[key]) for key in ("p", "m", "v")}
+
+        def check(t):
+            n = wl.numel[t]
+            lo, hi = off[t], off[t] + n
+            st = states[t]
+            c = ref.warmup_step(st["p"], st["m"], st["v"], np.ascontiguousarray(g[:, lo:hi]), wl.beta1, beta2,
+                                lr, wl.eps)
+            bad = [key for key in ("p", "m", "v") if not _same(c[key], got[key][lo:hi])]
+            states[t] = c
+            return t, bad, 3 * n
+
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            results = list(pool.map(check, sorted(range(wl.num_tensors), key=lambda t: -wl.numel[t])))
+        failed = [(wl.tensors[t][0], bad) for t, bad, _ in results if bad]
+        floats += sum(r[2] for r in results)
+        assert not failed, f"{name} warmup step {k}: {len(failed)} tensors differ, first {failed[:3]}"
+        log(f"{name} warmup step {k}: {floats} floats compared, all bit-identical")
         del got, g

@@ -206,3 +206,42 @@ def test_single_tensor_workload_trajectory_equals_numpy_oracle():
             assert _same(c[key], getattr(out.state, key)), (k, key)
         st = out.state
         cst = {key: c[key] for key in ("p", "m", "err_s", "err_w")}
+
+
+@pytest.mark.parametrize("n,W,dtype", [(1, 1, "f32"), (65, 3, "f32"), (1000, 8, "f32"), (777, 8, "bf16"),
+                                       (300, 64, "f32")])
+def test_warmup_equals_numpy_oracle(n, W, dtype):
+    """Three chained warmup steps from zero moments: p, m, v bit-identical."""
+    rng = _rng(2000 + n + W)
+    st = ob.TensorState(p=rng.normal(0, 0.02, n).astype(np.float32), m=np.zeros(n, np.float32),
+                        v=np.zeros(n, np.float32), err_s=np.zeros(n, np.float32),
+                        err_w=np.zeros((W, n), np.float32))
+    c = {"p": st.p.copy(), "m": st.m.copy(), "v": st.v.copy()}
+    for k in range(3):
+        g = rng.normal(0, 1e-3, (W, n)).astype(np.float32)
+        if dtype == "bf16":
+            g = (g.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        st = ob.warmup_step(st, g, 0.9, 0.999, 1e-3, 1e-8)
+        c = ref.warmup_step(c["p"], c["m"], c["v"], g, 0.9, 0.999, 1e-3, 1e-8)
+        for key in ("p", "m", "v"):
+            assert _same(c[key], getattr(st, key)), (k, key)
+
+
+def test_warmup_moments_match_torch_adam():
+    """The C++ warmup's m and v equal torch.optim.Adam's exp_avg and exp_avg_sq
+    on the averaged gradient (torch's lerp form rounds differently: 1e-5 rel)."""
+    import torch
+    rng = _rng(16)
+    n, W = 300, 4
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    c = {"p": p0.copy(), "m": np.zeros(n, np.float32), "v": np.zeros(n, np.float32)}
+    tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+    opt = torch.optim.Adam([tp], lr=1e-3, betas=(0.9, 0.999), eps=1e-8)
+    for _ in range(4):
+        g = (rng.standard_normal((W, n)) * 1e-3).astype(np.float32)
+        c = ref.warmup_step(c["p"], c["m"], c["v"], g, 0.9, 0.999, 1e-3, 1e-8)
+        tp.grad = torch.from_numpy(g.astype(np.float64).mean(axis=0).astype(np.float32))
+        opt.step()
+        s = opt.state[tp]
+        assert np.allclose(c["m"], s["exp_avg"].numpy(), rtol=1e-5, atol=1e-10)
+        assert np.allclose(c["v"], s["exp_avg_sq"].numpy(), rtol=1e-5, atol=1e-14)
