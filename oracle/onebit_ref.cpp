@@ -1,5 +1,6 @@
 // Plain, single-threaded C++ oracle of one compression-phase step of 1-bit
-// Adam, and of one warmup-phase (uncompressed Adam) step, for one tensor.
+// Adam, of one warmup-phase (uncompressed Adam) step, and of one exchange of
+// ScaleCom's cyclic local top-k codec, for one tensor.
 //
 // TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the
 // build entry module and the CPU-baseline leg of the benchmark load this
@@ -33,9 +34,11 @@
 // Every fp32 product and sum below is its own statement and the file is
 // compiled with -ffp-contract=off, so each rounds once.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <numeric>
 #include <vector>
 
 namespace {
@@ -253,6 +256,49 @@ int ref_warmup_step(int64_t n, int32_t W, const float *g, double beta1, double b
     const float step = lr32 * u;
     p[i] = p[i] - step;
   }
+  return 0;
+}
+
+// One exchange of the cyclic local top-k codec of the ScaleCom review (Proposed
+// method: a leader chosen cyclically picks the top-k indices, which every
+// worker then uses) with plain error feedback (R15): x_w = mem_w + g_w (fp32);
+// the leader is worker step mod W; the index set is the k positions of largest
+// |x_leader|, ties to the lower position, listed in ascending order; worker w
+// sends x_w there and keeps x_w with those positions zeroed as its memory; the
+// server averages the W messages (ascending fp32 sum from +0, then / W).
+//   g [W][n] fp32; memory [W][n] read and overwritten; index [k] (positions
+//   within the tensor), values [W][k] and average [k] written.
+// Returns 0, or 1 for a bad argument (k outside [1, n]).
+int ref_cltk_step(int64_t n, int32_t W, int64_t step, int64_t k, const float *g, float *memory,
+                  int64_t *index, float *values, float *average) {
+  if (n < 1 || W < 1 || k < 1 || k > n || step < 0 || !g || !memory || !index || !values || !average) return 1;
+  std::vector<float> x(static_cast<size_t>(W) * n);
+  for (size_t i = 0; i < x.size(); ++i) x[i] = memory[i] + g[i];
+  const float *lead = x.data() + static_cast<size_t>(step % W) * n;
+  // the k first positions in the order (|x_leader| descending, position ascending)
+  std::vector<int64_t> order(static_cast<size_t>(n));
+  std::iota(order.begin(), order.end(), int64_t{0});
+  auto before = [&](int64_t a, int64_t b) {
+    const float ka = std::fabs(lead[a]), kb = std::fabs(lead[b]);
+    return ka > kb || (ka == kb && a < b);
+  };
+  std::nth_element(order.begin(), order.begin() + (k - 1), order.end(), before);
+  std::sort(order.begin(), order.begin() + k);   // ascending positions
+  const float wf = static_cast<float>(W);
+  for (int64_t j = 0; j < k; ++j) {
+    const int64_t i = order[j];
+    index[j] = i;
+    float acc = 0.0f;
+    for (int32_t w = 0; w < W; ++w) {
+      const float xv = x[static_cast<size_t>(w) * n + i];
+      values[static_cast<size_t>(w) * k + j] = xv;
+      acc = acc + xv;
+    }
+    average[j] = acc / wf;
+  }
+  for (size_t i = 0; i < x.size(); ++i) memory[i] = x[i];
+  for (int64_t j = 0; j < k; ++j)
+    for (int32_t w = 0; w < W; ++w) memory[static_cast<size_t>(w) * n + order[j]] = 0.0f;
   return 0;
 }
 

@@ -1,5 +1,6 @@
 """ctypes front of the C++ oracle (oracle/onebit_ref.cpp): one compression-phase
-step and one warmup step of one tensor, plain and single-threaded.
+step, one warmup step and one cyclic-local-top-k exchange of one tensor, plain
+and single-threaded.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the build
 entry module and the CPU-baseline leg of the benchmark may import this module.
@@ -67,6 +68,9 @@ def load() -> ctypes.CDLL:
     lib.ref_warmup_step.restype = ctypes.c_int
     lib.ref_warmup_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p]
+    lib.ref_cltk_step.restype = ctypes.c_int
+    lib.ref_cltk_step.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _f32p, _f32p,
+                                  np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS"), _f32p, _f32p]
     _lib = lib
     return lib
 
@@ -129,4 +133,19 @@ def warmup_step(p, m, v, grads, beta1: float, beta2: float, lr: float, eps: floa
                                 out["p"], out["m"], out["v"])
     if st != 0:
         raise ValueError("ref_warmup_step rejected its arguments")
+    return out
+
+
+def cltk_step(memory, grads, step: int, k: int) -> dict:
+    """One cyclic-local-top-k exchange of one tensor on a copy of the memories
+    [W][n]; grads [W][n] fp32 or bf16 bit patterns.  Returns index (int64 [k],
+    ascending), values [W][k], average [k] and the new memory [W][n]."""
+    g = np.ascontiguousarray(widen(np.asarray(grads)))
+    W, n = g.shape
+    out = {"memory": _f32(memory).reshape(W, n).copy(), "index": np.zeros(k, dtype=np.int64),
+           "values": np.zeros((W, k), dtype=np.float32), "average": np.zeros(k, dtype=np.float32)}
+    st = load().ref_cltk_step(n, W, int(step), int(k), g, out["memory"], out["index"], out["values"],
+                              out["average"])
+    if st != 0:
+        raise ValueError("ref_cltk_step rejected its arguments")
     return out

@@ -7,7 +7,8 @@ GPT-1.3B-shaped list with bf16 gradients (W = 8).  After every step each
 tensor's sign words, scales, materialized errors, momentum and parameters are
 compared bit for bit with the C++ oracle's step, which runs on host copies of
 the same inputs and carries its own state from step to step.  The warmup step
-(uncompressed Adam) likewise on the BERT-Large and GPT-1.3B lists.  The oracle
+(uncompressed Adam) likewise on the BERT-Large and GPT-1.3B lists, and the
+cyclic local top-k exchange on the BERT-Large and ResNet-50 lists.  The oracle
 runs one tensor per call from a pool of host threads.  The C++ oracle
 (oracle/onebit_ref.cpp) is pinned on the CPU by tests/test_oracle_cpp.py.
 """
@@ -146,3 +147,55 @@ def test_warmup_every_element_against_cpp_oracle(name, steps):
         assert not failed, f"{name} warmup step {k}: {len(failed)} tensors differ, first {failed[:3]}"
         log(f"{name} warmup step {k}: {floats} floats compared, all bit-identical")
         del got, g
+
+
+@pytest.mark.parametrize("name,steps", [("bert_large", 3), ("resnet50_w32", 3)])
+def test_cltk_every_element_against_cpp_oracle(name, steps):
+    """The cyclic local top-k exchange at density 0.01 from zero memories (the
+    first exchange without a threshold prediction, then the predicted window and
+    its fallback), every index, value, average and memory element bit for bit."""
+    from error_compensated_bit_02_amd import OneBitAdam
+    density = 0.01
+    wl = WORKLOADS[name]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    log(f"{name}: {steps} CLT-k exchanges, every tensor against the C++ oracle ({threads} threads)")
+    ref.load()
+    ctx = OneBitAdam(wl.numel, wl.workers, wl.grad_dtype, wl.beta1, wl.eps)
+    k_off = ctx.cltk_configure(density)
+    run_off = ctx.offsets
+    memory = torch.zeros(wl.workers, ctx.N, device="cuda")
+    index = torch.zeros(ctx.K, dtype=torch.int32, device="cuda")
+    values = torch.zeros(wl.workers, ctx.K, device="cuda")
+    average = torch.zeros(ctx.K, device="cuda")
+    mems = [np.zeros((wl.workers, n), np.float32) for n in wl.numel]
+    gbuf = None
+    compared = 0
+    for k in range(steps):
+        gbuf = grads_for_step(wl, k, "cuda", out=gbuf)
+        g = _host(gbuf)
+        ctx.cltk_step(k, gbuf, memory, index, values, average)
+        torch.cuda.synchronize()
+        got = {"memory": _host(memory), "index": _host(index), "values": _host(values), "average": _host(average)}
+
+        def check(t):
+            n = wl.numel[t]
+            lo, hi = run_off[t], run_off[t] + n
+            klo, khi = k_off[t], k_off[t + 1]
+            c = ref.cltk_step(mems[t], np.ascontiguousarray(g[:, lo:hi]), k, khi - klo)
+            bad = [key for key, mine, dev in (
+                ("index", c["index"], got["index"][klo:khi].astype(np.int64)),
+                ("values", c["values"], got["values"][:, klo:khi]),
+                ("average", c["average"], got["average"][klo:khi]),
+                ("memory", c["memory"], got["memory"][:, lo:hi]),
+            ) if not _same(mine, dev)]
+            mems[t] = c["memory"]
+            return t, bad, (khi - klo) * (2 + wl.workers) + wl.workers * n
+
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            results = list(pool.map(check, sorted(range(wl.num_tensors), key=lambda t: -wl.numel[t])))
+        failed = [(wl.tensors[t][0], bad) for t, bad, _ in results if bad]
+        compared += sum(r[2] for r in results)
+        assert not failed, f"{name} exchange {k}: {len(failed)} tensors differ, first {failed[:3]}"
+        log(f"{name} exchange {k}: {compared} entries compared, all bit-identical")
+        del got, g
+    ctx.close()

@@ -245,3 +245,57 @@ def test_warmup_moments_match_torch_adam():
         s = opt.state[tp]
         assert np.allclose(c["m"], s["exp_avg"].numpy(), rtol=1e-5, atol=1e-10)
         assert np.allclose(c["v"], s["exp_avg_sq"].numpy(), rtol=1e-5, atol=1e-14)
+
+
+def test_cltk_golden_worked_example():
+    """The hand-derived two-exchange CLT-k example in tests/golden/ (ties at the
+    selection boundary in both steps, the leader moving from worker 0 to 1)."""
+    g = load("cltk_worked.txt")
+    k = ints(g["k"])[0]
+    f = lambda key: np.array(floats(g[key]), dtype=np.float32)  # noqa: E731
+    mem = np.zeros((3, 6), np.float32)
+    for step in (0, 1):
+        grads = np.stack([f(f"step{step}.g{w}") for w in range(3)])
+        c = ref.cltk_step(mem, grads, step, k)
+        assert c["index"].tolist() == ints(g[f"step{step}.index"]), step
+        for w in range(3):
+            assert c["values"][w].tolist() == floats(g[f"step{step}.values{w}"]), (step, w)
+            assert c["memory"][w].tolist() == floats(g[f"step{step}.mem{w}"]), (step, w)
+        assert c["average"].tolist() == floats(g[f"step{step}.average"]), step
+        mem = c["memory"]
+
+
+def test_cltk_equals_numpy_oracle_with_ties():
+    """Random small tensors drawn from a few values (many ties, -0 and +0), random
+    k and leader, chained exchanges: every output bit-identical to the numpy
+    oracle's, which is itself pinned to a pure-Python sort."""
+    rng = _rng(22)
+    for _ in range(40):
+        W, n = int(rng.integers(1, 6)), int(rng.integers(1, 200))
+        mem = rng.choice(np.array([-2, -1, -0.0, 0, 1, 2, 3], np.float32), (W, n))
+        for step in range(3):
+            g = rng.choice(np.array([-1, 0, 1, 0.5, -0.0], np.float32), (W, n))
+            k = int(rng.integers(1, n + 1))
+            o = ob.cltk_step(mem, g, step, k)
+            c = ref.cltk_step(mem, g, step, k)
+            assert np.array_equal(c["index"], o.index)
+            for key, want in (("values", o.values), ("average", o.average), ("memory", o.memory)):
+                assert _same(c[key], want), key
+            mem = o.memory
+
+
+@pytest.mark.parametrize("n,W,density,dtype", [(8193, 4, 0.01, "f32"), (20000, 8, 0.1, "bf16"), (777, 3, 1.0, "f32")])
+def test_cltk_equals_numpy_oracle_random(n, W, density, dtype):
+    rng = _rng(3000 + n)
+    mem = rng.normal(0, 1e-3, (W, n)).astype(np.float32)
+    k = ob.cltk_k(n, density)
+    for step in range(4):
+        g = rng.normal(0, 1e-3, (W, n)).astype(np.float32)
+        if dtype == "bf16":
+            g = (g.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        o = ob.cltk_step(mem, g, step, k)
+        c = ref.cltk_step(mem, g, step, k)
+        assert np.array_equal(c["index"], o.index)
+        for key, want in (("values", o.values), ("average", o.average), ("memory", o.memory)):
+            assert _same(c[key], want), (step, key)
+        mem = o.memory
