@@ -18,6 +18,10 @@ void ref_pack_signs(const float *x, int64_t n, uint64_t *words);
 int ref_compression_step(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
                          float *p, float *m, const float *v, float *err_s, float *err_w,
                          uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s);
+int ref_warmup_step(int64_t n, int32_t W, const float *g, double beta1, double beta2, double lr, double eps,
+                    float *p, float *m, float *v);
+int ref_cltk_step(int64_t n, int32_t W, int64_t step, int64_t k, const float *g, float *memory,
+                  int64_t *index, float *values, float *average);
 }
 
 static int failures = 0;
@@ -61,6 +65,23 @@ int main() {
           const bool bit = (ps[i / 64] >> (i % 64)) & 1u;
           expect(m[i] == (bit ? ss[0] : -ss[0]), "momentum", n, i);
         }
+      }
+    }
+  }
+  // the warmup step and the CLT-k exchange on the same sizes, every k from 1 to n for small n
+  for (int64_t n : sizes) {
+    for (int32_t W = 1; W <= 9; W += 4) {
+      std::vector<float> g(static_cast<size_t>(W * n)), p(n, 0.5f), m(n, 0.0f), v(n, 0.0f),
+          mem(static_cast<size_t>(W * n), 0.0f);
+      for (size_t i = 0; i < g.size(); ++i) g[i] = (i % 5 == 0) ? 0.0f : normal(rng);   // ties at 0
+      expect(ref_warmup_step(n, W, g.data(), 0.9, 0.999, 1e-3, 1e-8, p.data(), m.data(), v.data()) == 0,
+             "warmup status", n, W);
+      for (int64_t k = 1; k <= n; k += (n < 70 ? 1 : n / 7)) {
+        std::vector<int64_t> index(k);
+        std::vector<float> values(static_cast<size_t>(W * k)), average(k);
+        expect(ref_cltk_step(n, W, k, k, g.data(), mem.data(), index.data(), values.data(), average.data()) == 0,
+               "cltk status", n, k);
+        for (int64_t j = 1; j < k; ++j) expect(index[j - 1] < index[j], "cltk index ascending", n, j);
       }
     }
   }
