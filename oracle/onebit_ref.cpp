@@ -29,6 +29,8 @@
 //   momentum after the step: the server's reconstruction               (R7)
 //   update    p - lr*(m/(sqrt(v)+eps)), fp32, correctly rounded       (R8)
 //   a NaN or Inf anywhere in a tensor makes its scale NaN              (R9)
+//   partitioned server: one scale per chunk of whole 8192-element blocks (R11)
+//   1-bit LAMB's layer-wise trust ratio on the update                  (R14)
 //   warmup    Adam on the R6 average of the gradients, v with
 //             b2 = fp32(beta2), cb2 = fp32(1 - beta2), no bias correction (R10)
 // Every fp32 product and sum below is its own statement and the file is
@@ -157,19 +159,26 @@ float ref_scale(const float *x, int64_t n) { return onebit_scale(x, n); }
 
 void ref_pack_signs(const float *x, int64_t n, uint64_t *words) { pack_signs(x, n, words); }
 
-// One compression-phase step of one tensor of n elements with W workers.
+// One compression-phase step of one tensor of n elements with W workers, with
+// the server partitioned into C chunks (R11: chunk j covers [j*S, min((j+1)*S,
+// n)), S = 8192*ceil(ceil(n/8192)/C), each with its own scale; C = 1 is one
+// scale per tensor) and, when trust != 0, the update scaled by the layer-wise
+// trust ratio of 1-bit LAMB (R14: u = m/(sqrt(v)+eps), plus wd*p when wd > 0;
+// r = fp32(sqrt(fl64(sum p^2)) / sqrt(fl64(sum u^2))), 1 when a sum is 0;
+// p - lr*(r*u)).
 //   g        [W][n] fp32 gradients (bf16 gradients widened by the caller: exact)
 //   p, m     [n] parameters and the shared momentum, read and overwritten
 //   v        [n] frozen variance
 //   err_s    [n] server error, read and overwritten
 //   err_w    [W][n] worker errors, read and overwritten
 //   packed_w [W][ceil(n/64)] and scale_w [W]: the worker messages (written)
-//   packed_s [ceil(n/64)] and scale_s [1]: the server message (written)
-// Returns 0, or 1 for a bad argument (n < 1, W < 1, a null pointer).
-int ref_compression_step(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
-                         float *p, float *m, const float *v, float *err_s, float *err_w,
-                         uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s) {
-  if (n < 1 || W < 1 || !g || !p || !m || !v || !err_s || !err_w || !packed_w || !scale_w ||
+//   packed_s [ceil(n/64)] and scale_s [chunks]: the server message (written)
+// Returns 0, or 1 for a bad argument (n < 1, W < 1, C < 1, a null pointer).
+int ref_compression_step_opts(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
+                              int32_t chunks, int32_t trust, double wd, float *p, float *m, const float *v,
+                              float *err_s, float *err_w, uint64_t *packed_w, float *scale_w,
+                              uint64_t *packed_s, float *scale_s) {
+  if (n < 1 || W < 1 || chunks < 1 || !g || !p || !m || !v || !err_s || !err_w || !packed_w || !scale_w ||
       !packed_s || !scale_s)
     return 1;
   const int64_t nw = (n + 63) / 64;
@@ -203,23 +212,52 @@ int ref_compression_step(int64_t n, int32_t W, const float *g, double beta1, dou
     const float y = acc / wf;
     x[i] = y + err_s[i];
   }
-  const float ss = onebit_scale(x.data(), n);
+  // the server's message: signs of every element, one scale per chunk
+  const int64_t blocks = (n + 8191) / 8192;
+  const int64_t chunk = 8192 * ((blocks + chunks - 1) / chunks);
+  for (int64_t lo = 0; lo < n; lo += chunk) {
+    const int64_t hi = lo + chunk < n ? lo + chunk : n;
+    scale_s[lo / chunk] = onebit_scale(x.data() + lo, hi - lo);
+  }
   pack_signs(x.data(), n, packed_s);
-  scale_s[0] = ss;
 
-  // server error, momentum = the server's reconstruction, preconditioned update
-  const float lr32 = static_cast<float>(lr);
+  // server error and momentum = the server's reconstruction
+  std::vector<float> u(static_cast<size_t>(n));
   const float eps32 = static_cast<float>(eps);
+  const float wd32 = static_cast<float>(wd);
   for (int64_t i = 0; i < n; ++i) {
-    const float mhat = decompressed(packed_s, ss, i);
+    const float mhat = decompressed(packed_s, scale_s[i / chunk], i);
     err_s[i] = x[i] - mhat;
     m[i] = mhat;
     const float d = std::sqrt(v[i]) + eps32;
-    const float u = mhat / d;
-    const float step = lr32 * u;
+    u[i] = mhat / d;
+    if (trust && wd > 0.0) {
+      const float t = wd32 * p[i];
+      u[i] = u[i] + t;
+    }
+  }
+  // preconditioned update, scaled by the trust ratio when asked
+  const float lr32 = static_cast<float>(lr);
+  float r = 1.0f;
+  if (trust) {
+    const double sp = exact_sum_of_squares(p, n);
+    const double su = exact_sum_of_squares(u.data(), n);
+    r = (sp == 0.0 || su == 0.0) ? 1.0f : static_cast<float>(std::sqrt(sp) / std::sqrt(su));
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    const float ru = trust ? r * u[i] : u[i];
+    const float step = lr32 * ru;
     p[i] = p[i] - step;
   }
   return 0;
+}
+
+// The step with one server scale per tensor and the plain update.
+int ref_compression_step(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
+                         float *p, float *m, const float *v, float *err_s, float *err_w,
+                         uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s) {
+  return ref_compression_step_opts(n, W, g, beta1, lr, eps, 1, 0, 0.0, p, m, v, err_s, err_w, packed_w,
+                                   scale_w, packed_s, scale_s);
 }
 
 // One warmup-phase step of one tensor: full-precision Adam on the workers'

@@ -65,6 +65,11 @@ def load() -> ctypes.CDLL:
     lib.ref_compression_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double,
                                          ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p, _f32p,
                                          _f32p, _u64p, _f32p, _u64p, _f32p]
+    lib.ref_compression_step_opts.restype = ctypes.c_int
+    lib.ref_compression_step_opts.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double,
+                                              ctypes.c_double, ctypes.c_double, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_double, _f32p, _f32p, _f32p, _f32p, _f32p, _u64p, _f32p,
+                                              _u64p, _f32p]
     lib.ref_warmup_step.restype = ctypes.c_int
     lib.ref_warmup_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p]
@@ -103,23 +108,31 @@ def widen(g: np.ndarray) -> np.ndarray:
     return _f32(g)
 
 
-def compression_step(p, m, v, err_s, err_w, grads, beta1: float, lr: float, eps: float) -> dict:
+def compression_step(p, m, v, err_s, err_w, grads, beta1: float, lr: float, eps: float,
+                     server_chunks: int = 1, trust_wd=None) -> dict:
     """One step of one tensor on copies of the state.  grads [W][n] (fp32 or
     bf16 bit patterns).  Returns the new p, m, err_s, err_w and the messages:
-    packed_w [W][ceil(n/64)], scale_w [W], packed_s [ceil(n/64)], scale_s (fp32)."""
+    packed_w [W][ceil(n/64)], scale_w [W], packed_s [ceil(n/64)], scales_s (fp32,
+    one per server chunk) and scale_s (the first).  server_chunks = C > 1
+    partitions the server (R11); trust_wd, when not None, scales the update by
+    the trust ratio with that weight decay (R14)."""
     g = np.ascontiguousarray(widen(np.asarray(grads)))
     W, n = g.shape
     nw = (n + 63) // 64
+    blocks = -(-n // 8192)
+    pieces = -(-n // (8192 * -(-blocks // int(server_chunks))))
     out = {"p": _f32(p).copy(), "m": _f32(m).copy(), "err_s": _f32(err_s).copy(),
            "err_w": _f32(err_w).reshape(W, n).copy(),
            "packed_w": np.zeros((W, nw), dtype=np.uint64), "scale_w": np.zeros(W, dtype=np.float32),
-           "packed_s": np.zeros(nw, dtype=np.uint64), "scale_s": np.zeros(1, dtype=np.float32)}
-    st = load().ref_compression_step(n, W, g, float(beta1), float(lr), float(eps), out["p"], out["m"],
-                                     _f32(v), out["err_s"], out["err_w"], out["packed_w"],
-                                     out["scale_w"], out["packed_s"], out["scale_s"])
+           "packed_s": np.zeros(nw, dtype=np.uint64), "scales_s": np.zeros(pieces, dtype=np.float32)}
+    st = load().ref_compression_step_opts(n, W, g, float(beta1), float(lr), float(eps), int(server_chunks),
+                                          0 if trust_wd is None else 1,
+                                          0.0 if trust_wd is None else float(trust_wd), out["p"], out["m"],
+                                          _f32(v), out["err_s"], out["err_w"], out["packed_w"],
+                                          out["scale_w"], out["packed_s"], out["scales_s"])
     if st != 0:
-        raise ValueError("ref_compression_step rejected its arguments")
-    out["scale_s"] = out["scale_s"][0]
+        raise ValueError("ref_compression_step_opts rejected its arguments")
+    out["scale_s"] = out["scales_s"][0]
     return out
 
 

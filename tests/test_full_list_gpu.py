@@ -3,7 +3,8 @@
 The benchmark's launch configuration (the residual-form step over the whole
 list, one launch per kernel) on the BERT-Large-shaped list (W = 8), the
 ResNet-50-shaped list (W = 32), the BERT-base-shaped list (W = 64) and the
-GPT-1.3B-shaped list with bf16 gradients (W = 8).  After every step each
+GPT-1.3B-shaped list with bf16 gradients (W = 8), and the BERT-Large list with
+the server partitioned 8 ways and with the trust-ratio update.  After every step each
 tensor's sign words, scales, materialized errors, momentum and parameters are
 compared bit for bit with the C++ oracle's step, which runs on host copies of
 the same inputs and carries its own state from step to step.  The warmup step
@@ -47,14 +48,21 @@ def _same(a, b) -> bool:
     return a.shape == b.shape and np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,steps", [("resnet50_w32", 3), ("bert_large", 2), ("bert_base_w64", 1),
-                                        ("gpt_1p3b_bf16", 1)])
-def test_every_element_against_cpp_oracle(name, steps):
+CASES = [("resnet50_w32", 3, 1, None), ("bert_large", 2, 1, None), ("bert_base_w64", 1, 1, None),
+         ("gpt_1p3b_bf16", 1, 1, None),
+         ("bert_large", 2, 8, None),     # the server partitioned 8 ways
+         ("bert_large", 2, 1, 0.01)]     # the trust-ratio update with weight decay
+CASE_IDS = ["resnet50_w32", "bert_large", "bert_base_w64", "gpt_1p3b_bf16", "bert_large_server8", "bert_large_trust"]
+
+
+@pytest.mark.parametrize("name,steps,chunks,trust_wd", CASES, ids=CASE_IDS)
+def test_every_element_against_cpp_oracle(name, steps, chunks, trust_wd):
     wl = WORKLOADS[name]
     threads = max(1, min(16, os.cpu_count() or 1))
-    log(f"{name}: {steps} residual-form steps, every tensor against the C++ oracle ({threads} threads)")
+    log(f"{name}: {steps} residual-form steps (server chunks {chunks}, trust-ratio weight decay "
+        f"{trust_wd}), every tensor against the C++ oracle ({threads} threads)")
     ref.load()
-    run = Run(wl)
+    run = Run(wl, server_chunks=chunks, trust_wd=trust_wd)
     off, W = run.off, wl.workers
     host = {k: _host(run.state[k]) for k in ("p", "m", "v", "err_s", "err_w")}
     # the oracle's own state, per tensor
@@ -83,17 +91,18 @@ def test_every_element_against_cpp_oracle(name, steps):
             wlo, whi = lo // 64, lo // 64 + (n + 63) // 64
             st = states[t]
             c = ref.compression_step(st["p"], st["m"], st["v"], st["err_s"], st["err_w"],
-                                     np.ascontiguousarray(g[:, lo:hi]), wl.beta1, wl.lr, wl.eps)
+                                     np.ascontiguousarray(g[:, lo:hi]), wl.beta1, wl.lr, wl.eps,
+                                     server_chunks=chunks, trust_wd=trust_wd)
             bad = [key for key, mine, dev in (
                 ("packed_w", c["packed_w"], got["packed_w"][:, wlo:whi]),
                 ("scale_w", c["scale_w"], got["scale_w"][:, t]),
                 ("packed_s", c["packed_s"], got["packed_s"][wlo:whi]),
-                ("scale_s", np.float32(c["scale_s"]), got["scale_s"][t]),
+                ("scale_s", c["scales_s"], got["scale_s"][run.piece_base[t]:run.piece_base[t + 1]]),
                 ("p", c["p"], got["p"][lo:hi]), ("m", c["m"], got["m"][lo:hi]),
                 ("err_s", c["err_s"], got["err_s"][lo:hi]), ("err_w", c["err_w"], got["err_w"][:, lo:hi]),
             ) if not _same(mine, dev)]
             states[t] = {"p": c["p"], "m": c["m"], "v": st["v"], "err_s": c["err_s"], "err_w": c["err_w"]}
-            return t, bad, W * ((n + 63) // 64) + (n + 63) // 64, (3 + W) * n + W + 1
+            return t, bad, W * ((n + 63) // 64) + (n + 63) // 64, (3 + W) * n + W + c["scales_s"].size
 
         with ThreadPoolExecutor(max_workers=threads) as pool:
             results = list(pool.map(check, sorted(range(wl.num_tensors), key=lambda t: -wl.numel[t])))

@@ -299,3 +299,31 @@ def test_cltk_equals_numpy_oracle_random(n, W, density, dtype):
         for key, want in (("values", o.values), ("average", o.average), ("memory", o.memory)):
             assert _same(c[key], want), (step, key)
         mem = o.memory
+
+
+@pytest.mark.parametrize("n,W,chunks,trust_wd", [(70001, 3, 2, None), (70001, 3, 8, None), (8193, 4, 3, None),
+                                                 (100, 2, 4, None), (20000, 3, 1, 0.0), (20000, 3, 1, 0.01),
+                                                 (70001, 2, 4, 0.01)])
+def test_partitioned_server_and_trust_ratio_equal_numpy_oracle(n, W, chunks, trust_wd):
+    """The server partitioned into chunks of whole 8192-element blocks, and the
+    trust-ratio update: three chained steps, every output bit-identical to the
+    numpy oracle's."""
+    rng = _rng(4000 + n + chunks)
+    st = ob.TensorState(p=rng.normal(0, 0.02, n).astype(np.float32), m=np.zeros(n, np.float32),
+                        v=(np.abs(rng.normal(0, 1e-3, n)) ** 2 + 1e-12).astype(np.float32),
+                        err_s=np.zeros(n, np.float32), err_w=np.zeros((W, n), np.float32))
+    cst = {"p": st.p.copy(), "m": st.m.copy(), "err_s": st.err_s.copy(), "err_w": st.err_w.copy()}
+    scomp = None if chunks == 1 else ob.ChunkedOneBitCompressor(chunks)
+    for k in range(3):
+        g = rng.normal(0, 1e-3, (W, n)).astype(np.float32)
+        out = ob.compression_step(st, g, 0.9, 1e-4, 1e-8, server_comp=scomp, trust_ratio_wd=trust_wd)
+        c = ref.compression_step(cst["p"], cst["m"], st.v, cst["err_s"], cst["err_w"], g, 0.9, 1e-4, 1e-8,
+                                 server_chunks=chunks, trust_wd=trust_wd)
+        words, scales = ob.words_of(out.worker_msgs)
+        assert _same(c["packed_w"], words) and _same(c["scale_w"], scales), k
+        want_ss = out.server_msg.scales if chunks > 1 else np.array([out.server_msg.scale], np.float32)
+        assert _same(c["packed_s"], out.server_msg.words) and _same(c["scales_s"], want_ss), k
+        for key in ("p", "m", "err_s", "err_w"):
+            assert _same(c[key], getattr(out.state, key)), (k, key)
+        st = out.state
+        cst = {key: c[key] for key in ("p", "m", "err_s", "err_w")}
