@@ -183,69 +183,106 @@ def summarize_counters(pmc_dir: str, workload: str) -> dict:
             "per_launch_write_bytes": {k: round(write.get(k, 0.0) * write_factor) for k in per}}
 
 
-def cpu_baseline(wl, state, grads, sample_tensors: int) -> dict:
-    """The C++ oracle (oracle/onebit_ref.cpp), as it stands, single-threaded, on
-    the first `sample_tensors` tensors for one step.  Inputs are copied to
-    host arrays before the clock starts; the timed region is the oracle's
-    step over those tensors."""
+def host_copy(t):
+    """The bits of a device tensor in a new host array (bf16 as uint16
+    patterns, int64 words as uint64), through a preallocated pageable buffer."""
     import numpy as np
-    import oracle.ref as ref
-    from synth import host_slice
-    from synth.workloads import padded_layout
-    lib = ref.load()
-    off, _ = padded_layout(wl.numel)
-    tensors = list(range(min(sample_tensors, wl.num_tensors)))
-    W = wl.workers
-    jobs = []
-    for t in tensors:
-        lo, hi = off[t], off[t] + wl.numel[t]
-        n, nw = hi - lo, (hi - lo + 63) // 64
-        f32 = lambda key: np.ascontiguousarray(host_slice(state[key], lo, hi), dtype=np.float32)  # noqa: E731
-        jobs.append((n, np.ascontiguousarray(ref.widen(host_slice(grads, lo, hi))), f32("p"), f32("m"), f32("v"),
-                     f32("err_s"), f32("err_w"), np.zeros((W, nw), np.uint64), np.zeros(W, np.float32),
-                     np.zeros(nw, np.uint64), np.zeros(1, np.float32)))
-    n_total = sum(job[0] for job in jobs)
-    # fresh copies of the state each run overwrites, for the all-cores run below
-    spare = [(n, g, p.copy(), m.copy(), v, es.copy(), ew.copy(), pw.copy(), sw.copy(), ps.copy(), ss.copy())
-             for n, g, p, m, v, es, ew, pw, sw, ps, ss in jobs]
+    import torch
+    bits = {torch.float32: (torch.float32, np.float32, np.float32),
+            torch.bfloat16: (torch.int16, np.int16, np.uint16),
+            torch.int64: (torch.int64, np.int64, np.uint64)}[t.dtype]
+    a = np.empty(tuple(t.shape), bits[2])
+    torch.from_numpy(a.view(bits[1])).copy_(t.view(bits[0]))
+    return a
 
-    def run(job):
-        n, g, p, m, v, es, ew, pw, sw, ps, ss = job
-        if lib.ref_compression_step(n, W, g, wl.beta1, wl.lr, wl.eps, p, m, v, es, ew, pw, sw, ps, ss) != 0:
-            raise RuntimeError("the C++ oracle rejected its arguments")
 
-    t0 = time.perf_counter()
-    for job in jobs:
-        run(job)
-    dt = time.perf_counter() - t0
-    # the same oracle on the host's cores (at most 16, one GPU's share), one tensor per call,
-    # largest first; ctypes releases the GIL during each call
-    from concurrent.futures import ThreadPoolExecutor
-    threads = max(1, min(16, os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as pool:
-        list(pool.map(run, sorted(spare, key=lambda job: -job[0])))
-    dt_all = time.perf_counter() - t0
-    cpu = "unknown"
+def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": n_total / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"C++ oracle, first {len(tensors)} tensors ({n_total} elements), 1 step, W={W}; "
-                      f"{dt:.1f} s on one core of {cpu}",
-            "seconds": dt,
-            "all_cores": {"value": n_total / dt_all, "unit": "elements/s", "cores": threads, "seconds": dt_all,
-                          "sample": f"the same tensors, one tensor per call, {threads} threads"}}
+    return "unknown"
 
 
-def time_form(form, wl, ctx, grads, steps, warmup, stream):
-    """Warmup, then `steps` timed steps of one state form from a fresh state.
-    Returns (seconds, {kernel: (total ms, launches)}) over the timed region."""
+def server_pieces(n: int, chunks: int) -> int:
+    """Server scales of an n-element tensor with the server split `chunks` ways
+    (whole 8192-element blocks per chunk)."""
+    blocks = -(-n // 8192)
+    return -(-n // (8192 * -(-blocks // chunks)))
+
+
+def cpu_baseline(wl, state, grads, server_chunks: int = 1, trust_wd=None, repeats: int = 5) -> dict:
+    """The C++ oracle (oracle/onebit_ref.cpp) as it stands, one compression
+    step over the whole tensor list on host copies of the benchmark's state
+    and one gradient set: first on one core (the calling thread pinned to the
+    first core it may run on), then `repeats` times from a pool of the host's
+    cores (at most 16 threads, one GPU's share; one tensor per call, largest
+    first), the median reported.  Each run continues the previous one's state
+    in place, as consecutive steps would.  Copies to the host are outside the
+    clocks."""
+    import numpy as np
+    import oracle.ref as ref
+    from concurrent.futures import ThreadPoolExecutor
+    from synth.workloads import padded_layout
+    lib = ref.load()
+    del lib
+    off, N = padded_layout(wl.numel)
+    W, T = wl.workers, wl.num_tensors
+    st = {k: host_copy(state[k]) for k in ("p", "m", "v", "err_s", "err_w")}
+    g = host_copy(grads)
+    pieces = [server_pieces(n, server_chunks) for n in wl.numel]
+    pbase = np.concatenate([[0], np.cumsum(pieces)]).astype(np.int64)
+    packed_w = np.zeros((W, N // 64), np.uint64)
+    scale_w = np.zeros((W, T), np.float32)
+    packed_s = np.zeros(N // 64, np.uint64)
+    scale_s = np.zeros(int(pbase[-1]), np.float32)
+
+    def run(t: int) -> None:
+        ref.compression_step_in_place(off[t], wl.numel[t], t, g, st["p"], st["m"], st["v"], st["err_s"],
+                                      st["err_w"], packed_w, scale_w, packed_s, scale_s[pbase[t]:pbase[t + 1]],
+                                      wl.beta1, wl.lr, wl.eps, server_chunks=server_chunks, trust_wd=trust_wd)
+
+    order = sorted(range(T), key=lambda t: -wl.numel[t])
+    n_total = sum(wl.numel)
+    allowed = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {allowed[0]})          # this thread only: one core
+    try:
+        t0 = time.perf_counter()
+        for t in order:
+            run(t)
+        dt1 = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    threads = max(1, min(16, len(allowed)))
+    runs = []
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            list(pool.map(run, order))
+            runs.append(time.perf_counter() - t0)
+    med = sorted(runs)[len(runs) // 2]
+    b_alg = step_bytes_per_element(wl)
+    cpu = cpu_model()
+    return {"value": n_total / dt1, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"the C++ oracle, one step over the whole list ({T} tensors, {n_total} elements, "
+                      f"W={W}), single-threaded and pinned to one core of {cpu}: {dt1:.1f} s",
+            "seconds": round(dt1, 3), "hbm_gbps_algorithmic": round(b_alg * n_total / dt1 / 1e9, 3),
+            "host_nproc": os.cpu_count(), "host_cores_allowed": len(allowed), "cpu_model": cpu,
+            "all_cores": {"value": n_total / med, "unit": "elements/s", "cores": threads, "repeats": repeats,
+                          "seconds_median": round(med, 3), "seconds_min": round(min(runs), 3),
+                          "seconds_max": round(max(runs), 3),
+                          "hbm_gbps_algorithmic": round(b_alg * n_total / med / 1e9, 2),
+                          "sample": f"the same step over the whole list, {threads} threads, one tensor per "
+                                    f"call; median of {repeats} runs"}}
+
+
+def time_form(form, wl, ctx, grads, steps, warmup, stream, repeats):
+    """Warmup, then `repeats` timed runs of exactly `steps` steps each of one
+    state form, continuing from a fresh state.  Returns ([seconds per run],
+    {kernel: (total ms, launches)} over every timed run, final state)."""
     import torch
     from synth import init_state
     st = init_state(wl, "cuda")
@@ -267,15 +304,18 @@ def time_form(form, wl, ctx, grads, steps, warmup, stream):
     torch.cuda.synchronize()
     ctx.profile(True)
     ctx.profile_read(reset=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(steps):
-        step(warmup + k)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    runs, k0 = [], warmup
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step(k0 + k)
+        torch.cuda.synchronize()
+        runs.append(time.perf_counter() - t0)
+        k0 += steps
     kernels = ctx.profile_read(reset=True)
     ctx.profile(False)
-    return dt, kernels, st
+    return runs, kernels, st
 
 
 def time_cltk(wl, ctx, grads, density, steps, warmup, stream):
@@ -425,12 +465,19 @@ def step_counter_gbps(workload, per_kernel, ms_step, steps):
     return round(total / (ms_step * 1e-3) / 1e9, 1)
 
 
-def summarize(wl, n_elem, steps, dt, kernels, workload):
+def summarize(wl, n_elem, steps, runs, kernels, workload):
+    """The step's figures from `runs` (seconds per timed run of `steps`
+    steps; the median is reported) and the kernels' event times over all runs."""
+    dt = sorted(runs)[len(runs) // 2]
     ms_step = dt * 1e3 / steps
     b_alg = step_bytes_per_element(wl)
     step_gbps = b_alg * n_elem / (ms_step * 1e-3) / 1e9
     per_kernel = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n} for k, (ms, n) in kernels.items()}
     kb = kernel_bytes_per_element(wl)
+    # bytes the form's own kernels move per element per step, each operand once per kernel
+    launches_per_step = {k: v["launches"] / (steps * len(runs)) for k, v in per_kernel.items()}
+    b_moved = sum(kb[k] * launches_per_step[k] for k in kb if per_kernel[k]["launches"])
+    moved_gbps = b_moved * n_elem / (ms_step * 1e-3) / 1e9
     dom = max((k for k in kb if per_kernel[k]["launches"]), key=lambda k: per_kernel[k]["avg_ms"])
     dom_ms = per_kernel[dom]["avg_ms"]
     achieved = kb[dom] * n_elem / (dom_ms * 1e-3) / 1e9
@@ -440,14 +487,22 @@ def summarize(wl, n_elem, steps, dt, kernels, workload):
                 "traffic": None if traffic is None else round(traffic),
                 "algorithmic_bytes": round(kb[dom] * n_elem),
                 "bytes_per_element": kb[dom], "avg_ms": round(dom_ms, 4)}
-    counter_gbps = step_counter_gbps(workload, per_kernel, ms_step, steps)
+    counter_gbps = step_counter_gbps(workload, per_kernel, ms_step, steps * len(runs))
     return {
         "ms_per_step": ms_step,
-        "value": n_elem * steps / dt,
+        "value": n_elem / (ms_step * 1e-3),
+        "repeats": len(runs),
+        "ms_per_step_min": round(min(runs) * 1e3 / steps, 4),
+        "ms_per_step_max": round(max(runs) * 1e3 / steps, 4),
         "step_hbm_gbps_algorithmic": round(step_gbps, 1),
         "step_hbm_gbps_counter": counter_gbps,
         "step_counter_frac_of_peak": None if counter_gbps is None else round(counter_gbps / HBM_PEAK_GBPS, 4),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "step_fraction": {"by_method_bytes": round(step_gbps / HBM_PEAK_GBPS, 4),
+                          "method_bytes_per_element": b_alg,
+                          "by_bytes_moved": round(moved_gbps / HBM_PEAK_GBPS, 4),
+                          "moved_bytes_per_element": round(b_moved, 4),
+                          "by_counters": None if counter_gbps is None else round(counter_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
         "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches": v["launches"]}
                     for k, v in per_kernel.items() if v["launches"]},
@@ -473,7 +528,8 @@ def main() -> int:
     ap.add_argument("--cltk-density", type=float, default=0.01,
                     help="also time the cyclic local top-k exchange keeping this fraction of "
                          "each tensor (0 = skip)")
-    ap.add_argument("--cpu-sample-tensors", type=int, default=256)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of --steps steps each per state form; the median is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/<workload>_hbm_counters.json from rocprofv3 --pmc runs "
@@ -533,10 +589,14 @@ def main() -> int:
     for form in forms:
         last_state = None
         torch.cuda.empty_cache()
-        dt, kernels, last_state = time_form(form, wl, ctx, grads, args.steps, args.warmup, stream)
-        results[form] = summarize(wl, n_elem, args.steps, dt, kernels, wl.name)
-        log(f"bench: {form}: {results[form]['ms_per_step']:.3f} ms/step, "
-            f"{100 * results[form]['step_frac_of_peak']:.1f}% of peak")
+        runs, kernels, last_state = time_form(form, wl, ctx, grads, args.steps, args.warmup, stream,
+                                              max(1, args.repeats))
+        results[form] = summarize(wl, n_elem, args.steps, runs, kernels, wl.name)
+        r = results[form]
+        log(f"bench: {form}: {r['ms_per_step']:.3f} ms/step (median of {r['repeats']} runs of "
+            f"{args.steps} steps; {r['ms_per_step_min']:.3f}-{r['ms_per_step_max']:.3f}), "
+            f"{100 * r['step_fraction']['by_method_bytes']:.1f}% of peak by the method's bytes, "
+            f"{100 * r['step_fraction']['by_bytes_moved']:.1f}% by the bytes moved")
 
     warm = None
     if not args.no_warmup_phase:
@@ -558,6 +618,8 @@ def main() -> int:
     result = {
         "metric": METRIC, "value": head["value"], "unit": "elements/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "repeats": head["repeats"], "ms_per_step_min": head["ms_per_step_min"],
+        "ms_per_step_max": head["ms_per_step_max"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "tensors": wl.num_tensors, "elements": n_elem,
@@ -569,6 +631,7 @@ def main() -> int:
         "step_hbm_gbps_counter": head["step_hbm_gbps_counter"],
         "step_counter_frac_of_peak": head["step_counter_frac_of_peak"],
         "step_bytes_per_element": step_bytes_per_element(wl),
+        "step_fraction": head["step_fraction"],
         "worker_elements_per_s": head["value"] * wl.workers,
         "roofline": head["roofline"],
         "kernels": head["kernels"],
@@ -586,7 +649,7 @@ def main() -> int:
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host (cpu baseline)")
-        result["cpu_baseline"] = cpu_baseline(wl, last_state, grads[0], args.cpu_sample_tensors)
+        result["cpu_baseline"] = cpu_baseline(wl, last_state, grads[0], args.server_chunks, args.trust_ratio)
     ctx.close()
     print(json.dumps(result), flush=True)
     return 0

@@ -69,13 +69,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 class OneBitError(RuntimeError):
-    pass
+    """A call of the C ABI returned a status other than OB_OK (in .status)."""
+
+    def __init__(self, message: str, status=None):
+        super().__init__(message)
+        self.status = status
 
 
 def _check(status: int, what: str) -> None:
     if status != OB_OK:
         msg = load_library().ob_status_string(status).decode()
-        raise OneBitError(f"{what}: {msg} (status {status})")
+        raise OneBitError(f"{what}: {msg} (status {status})", status)
 
 
 def layout(numel: Sequence[int]) -> List[int]:

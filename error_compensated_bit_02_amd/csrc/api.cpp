@@ -52,6 +52,8 @@ struct ob_ctx {
   double2 *partials = nullptr;     // (W+1) x num_tiles
   double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile (residual worker pass)
   bool profiling = false;
+  bool launched = false;             // some kernel was enqueued, on last_stream the latest
+  hipStream_t last_stream = nullptr;
   std::vector<EventPair> pending[ob::K_NUM_KINDS];
   std::vector<EventPair> pool;
 };
@@ -67,6 +69,7 @@ static_assert(sizeof(kKindNames) / sizeof(kKindNames[0]) == ob::K_NUM_KINDS,
               "one name per kernel kind");
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 
 int check_ptr(const void *p) {
   if (p == nullptr) return OB_ERR_INVALID;
@@ -89,9 +92,10 @@ int check_ptrs(const P *...ps) {
 // Brackets one launch with events when profiling is on.  On a failure the
 // event pair goes back to the pool.
 template <typename F>
-int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
+int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch, bool events = true) {
   EventPair ev;
-  if (c->profiling) {
+  const bool profiling = events && c->profiling;
+  if (profiling) {
     if (!c->pool.empty()) {
       ev = c->pool.back();
       c->pool.pop_back();
@@ -108,8 +112,10 @@ int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
     }
   }
   launch();
+  c->launched = true;
+  c->last_stream = s;
   const bool launched = hipGetLastError() == hipSuccess;
-  if (c->profiling) {
+  if (profiling) {
     if (!launched || hipEventRecord(ev.stop, s) != hipSuccess) {
       c->pool.push_back(ev);
       return OB_ERR_DEVICE;
@@ -118,6 +124,16 @@ int timed(ob_ctx *c, ob::Kind kind, hipStream_t s, F &&launch) {
   }
   return launched ? OB_OK : OB_ERR_DEVICE;
 }
+
+// Per-step scratch of one call: the context's own, or the static buffer of
+// the no-allocation step.
+struct StepScratch {
+  double2 *partials;         // (W+1) x num_tiles
+  double2 *chunk_partials;   // W x num_tiles * kChunksPerTile
+  float *ratio;              // [T]
+};
+
+StepScratch own_scratch(ob_ctx *c) { return StepScratch{c->partials, c->chunk_partials, c->d_ratio}; }
 
 ob::WorkerArgs worker_args(ob_ctx *c, int w0, int w1, const void *grads, const float *m,
                           float *err_w, uint64_t *packed_w, const float *scale_w,
@@ -189,53 +205,132 @@ int do_server_first(ob_ctx *c, const uint64_t *packed_w, const float *scale_w, f
 // trust ratio (two more launches: per-tile norms, per-tensor ratios).
 int do_update(ob_ctx *c, bool store_m, ob::Kind kind, const uint64_t *packed_s,
               const float *scale_s, const float *v, float *m, float *params, double lr,
-              hipStream_t s) {
+              hipStream_t s, const StepScratch &x, bool events = true) {
   const ob::UpdateArgs a{packed_s, scale_s, v, m, params, static_cast<float>(lr), c->eps,
-                         c->d_ratio, c->weight_decay};
+                         x.ratio, c->weight_decay};
   if (c->trust_ratio) {
-    int st = timed(c, ob::K_TRUST_NORMS, s, [&] { ob::launch_trust_norms(c->geo, a, c->partials, s); });
+    int st = timed(c, ob::K_TRUST_NORMS, s, [&] { ob::launch_trust_norms(c->geo, a, x.partials, s); }, events);
     if (st) return st;
-    st = timed(c, ob::K_TRUST_RATIO, s, [&] { ob::launch_trust_ratio(c->geo, c->partials, c->d_ratio, s); });
+    st = timed(c, ob::K_TRUST_RATIO, s, [&] { ob::launch_trust_ratio(c->geo, x.partials, x.ratio, s); },
+               events);
     if (st) return st;
   }
-  return timed(c, kind, s, [&] { ob::launch_update(store_m, c->trust_ratio, c->geo, a, s); });
+  return timed(c, kind, s, [&] { ob::launch_update(store_m, c->trust_ratio, c->geo, a, s); }, events);
+}
+
+// The residual-form step over the whole list with the given scratch; events
+// = false records no timing events (the no-allocation step creates none).
+int do_step_residual(ob_ctx *c, bool first, const void *grads, const float *m, const float *v,
+                     float *params, float *err_w, float *err_s, uint64_t *packed_w, float *scale_w,
+                     uint64_t *packed_s, float *scale_s, double lr, hipStream_t s, const StepScratch &x,
+                     bool events) {
+  const ob::Geometry &g = c->geo;
+  // worker: x = (c1*m + c2*g) + e, with e and m formed from the previous step's residual form
+  ob::WorkerArgs wa = worker_args(c, 0, c->W, grads, first ? m : nullptr, err_w, packed_w,
+                                  scale_w, packed_s, scale_s);
+  wa.partials = x.partials;
+  wa.chunk_partials = x.chunk_partials;
+  int r = timed(c, ob::K_WORKER_RESIDUAL, s, [&] {
+    ob::launch_worker(first ? ob::WorkerPass::kResidualFirst : ob::WorkerPass::kResidual, g,
+                      c->bf16, wa, s);
+  }, events);
+  if (r) return r;
+  r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
+    ob::launch_scale_finalize(g, x.chunk_partials, static_cast<int64_t>(g.num_tiles) * ob::kChunksPerTile,
+                              ob::kChunksPerTile, 0, c->W, g.tile_begin, g.numel, c->T, scale_w,
+                              static_cast<int64_t>(c->max_tensor_tiles) * ob::kChunksPerTile, s);
+  }, events);
+  if (r) return r;
+  ob::ServerArgs sa = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
+  sa.partials = x.partials;
+  r = timed(c, ob::K_SERVER_RESIDUAL, s, [&] {
+    ob::launch_server(first ? ob::ServerPass::kResidualFirst : ob::ServerPass::kResidual, g, sa, s);
+  }, events);
+  if (r) return r;
+  r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
+    ob::launch_scale_finalize(g, x.partials, g.num_tiles, 1, c->W, 1, g.piece_begin, g.piece_numel, c->S,
+                              scale_s, c->max_piece_tiles, s);
+  }, events);
+  if (r) return r;
+  return do_update(c, false, ob::K_UPDATE_RESIDUAL, packed_s, scale_s, v, nullptr, params, lr, s, x, events);
 }
 
 // Server pieces for a C-way partitioned server: chunk j of tensor t is a run
 // of q_t = ceil(k_t / C) of its k_t tiles (whole 8192-element tiles, the last
 // run shorter), so tensor t has ceil(k_t / q_t) <= C pieces.  C = 1 gives one
-// piece per tensor.  Uploads the three tables (synchronous copies).
-int upload_pieces(ob_ctx *c, int32_t chunks) {
-  std::vector<int32_t> tile_piece(c->num_tiles), piece_begin;
+// piece per tensor; any C at or above a tensor's tile count gives one piece
+// per tile.  Builds the three tables on the host, then uploads them
+// (synchronous copies).
+struct PieceTables {
+  std::vector<int32_t> tile_piece, piece_begin;
   std::vector<int64_t> piece_numel;
   int32_t max_piece = 0;
+};
+
+PieceTables build_pieces(const ob_ctx *c, int32_t chunks) {
+  PieceTables pt;
+  pt.tile_piece.resize(static_cast<size_t>(c->num_tiles));
   for (int32_t t = 0; t < c->T; ++t) {
-    const int32_t k = c->tile_begin[t + 1] - c->tile_begin[t];
-    const int32_t q = (k + chunks - 1) / chunks;
-    for (int32_t i = 0; i < k; i += q) {
-      const int32_t piece = static_cast<int32_t>(piece_begin.size());
-      piece_begin.push_back(c->tile_begin[t] + i);
-      const int64_t lo = static_cast<int64_t>(i) * ob::kTile;
-      const int64_t hi = std::min<int64_t>(static_cast<int64_t>(i + q) * ob::kTile, c->numel[t]);
-      piece_numel.push_back(hi - lo);
-      max_piece = std::max(max_piece, std::min(i + q, k) - i);
-      for (int32_t j = i; j < std::min(i + q, k); ++j) tile_piece[c->tile_begin[t] + j] = piece;
+    const int64_t k = c->tile_begin[t + 1] - c->tile_begin[t];
+    const int64_t q = (k + chunks - 1) / chunks;   // int64: chunks may be up to INT32_MAX
+    for (int64_t i = 0; i < k; i += q) {
+      const int32_t piece = static_cast<int32_t>(pt.piece_begin.size());
+      const int64_t end = std::min(i + q, k);
+      pt.piece_begin.push_back(c->tile_begin[t] + static_cast<int32_t>(i));
+      pt.piece_numel.push_back(std::min(end * ob::kTile, c->numel[t]) - i * ob::kTile);
+      pt.max_piece = std::max(pt.max_piece, static_cast<int32_t>(end - i));
+      for (int64_t j = i; j < end; ++j) pt.tile_piece[c->tile_begin[t] + j] = piece;
     }
   }
-  piece_begin.push_back(c->num_tiles);
-  const size_t S = piece_numel.size();
-  if (hipMemcpy(c->d_tile_piece, tile_piece.data(), tile_piece.size() * sizeof(int32_t),
+  pt.piece_begin.push_back(c->num_tiles);
+  return pt;
+}
+
+int copy_pieces(ob_ctx *c, const PieceTables &pt) {
+  if (hipMemcpy(c->d_tile_piece, pt.tile_piece.data(), pt.tile_piece.size() * sizeof(int32_t),
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(c->d_piece_begin, piece_begin.data(), piece_begin.size() * sizeof(int32_t),
+      hipMemcpy(c->d_piece_begin, pt.piece_begin.data(), pt.piece_begin.size() * sizeof(int32_t),
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(c->d_piece_numel, piece_numel.data(), S * sizeof(int64_t),
-                hipMemcpyHostToDevice) != hipSuccess)
+      hipMemcpy(c->d_piece_numel, pt.piece_numel.data(), pt.piece_numel.size() * sizeof(int64_t),
+                hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipGetLastError();
     return OB_ERR_DEVICE;
-  c->server_chunks = chunks;
-  c->max_piece_tiles = max_piece;
-  c->S = static_cast<int32_t>(S);
+  }
+  return OB_OK;
+}
+
+// Switches the server to `chunks` pieces per tensor.  If an upload fails, the
+// tables of the previous setting are uploaded again so the device tables and
+// the host's counts keep agreeing; the call still reports the failure.
+int upload_pieces(ob_ctx *c, int32_t chunks) {
+  const int32_t eff = std::min(chunks, std::max<int32_t>(1, c->max_tensor_tiles));
+  PieceTables pt;
+  try {
+    pt = build_pieces(c, eff);
+  } catch (const std::bad_alloc &) {
+    return OB_ERR_NOMEM;
+  }
+  if (copy_pieces(c, pt) != OB_OK) {
+    if (c->S > 0) {   // a configured context: restore what it held
+      try {
+        (void)copy_pieces(c, build_pieces(c, c->server_chunks));
+      } catch (const std::bad_alloc &) {
+      }
+    }
+    return OB_ERR_DEVICE;
+  }
+  c->server_chunks = eff;
+  c->max_piece_tiles = pt.max_piece;
+  c->S = static_cast<int32_t>(pt.piece_numel.size());
   c->geo.S = c->S;
   return OB_OK;
+}
+
+// Waits for the work this context last enqueued (the stream of its latest
+// launch) before its tables are rewritten; nothing else on the device waits.
+int wait_for_last_launch(ob_ctx *c) {
+  if (!c->launched) return OB_OK;
+  return hipStreamSynchronize(c->last_stream) == hipSuccess ? OB_OK : OB_ERR_DEVICE;
 }
 
 }  // namespace
@@ -431,7 +526,7 @@ int ob_apply_update(ob_ctx *c, const uint64_t *packed_s, const float *scale_s, c
   const int st = check_ptrs(packed_s, scale_s, v, m, params);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return do_update(c, true, ob::K_APPLY_UPDATE, packed_s, scale_s, v, m, params, lr, s);
+  return do_update(c, true, ob::K_APPLY_UPDATE, packed_s, scale_s, v, m, params, lr, s, own_scratch(c));
 }
 
 int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *params, float *err_w,
@@ -451,7 +546,7 @@ int ob_step(ob_ctx *c, const void *grads, float *m, const float *v, float *param
       ob::launch_server(ob::ServerPass::kStrictErrors, c->geo, a, s);
     });
     if (r) return r;
-    return do_update(c, true, ob::K_APPLY_UPDATE, packed_s, scale_s, v, m, params, lr, s);
+    return do_update(c, true, ob::K_APPLY_UPDATE, packed_s, scale_s, v, m, params, lr, s, own_scratch(c));
   }
   ob::ServerArgs a = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
   a.v = v;
@@ -470,33 +565,8 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   int st = check_ptrs(grads, v, params, err_w, err_s, packed_w, scale_w, packed_s, scale_s);
   if (st) return st;
   if (first && (st = check_ptr(m)) != OB_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const ob::Geometry &g = c->geo;
-  // worker: x = (c1*m + c2*g) + e, with e and m formed from the previous step's residual form
-  const ob::WorkerArgs wa = worker_args(c, 0, c->W, grads, first ? m : nullptr, err_w, packed_w,
-                                        scale_w, packed_s, scale_s);
-  int r = timed(c, ob::K_WORKER_RESIDUAL, s, [&] {
-    ob::launch_worker(first ? ob::WorkerPass::kResidualFirst : ob::WorkerPass::kResidual, g,
-                      c->bf16, wa, s);
-  });
-  if (r) return r;
-  r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    ob::launch_scale_finalize(g, c->chunk_partials, static_cast<int64_t>(g.num_tiles) * ob::kChunksPerTile,
-                              ob::kChunksPerTile, 0, c->W, g.tile_begin, g.numel, c->T, scale_w,
-                              static_cast<int64_t>(c->max_tensor_tiles) * ob::kChunksPerTile, s);
-  });
-  if (r) return r;
-  const ob::ServerArgs sa = server_args(c, packed_w, scale_w, err_s, scale_s, packed_s);
-  r = timed(c, ob::K_SERVER_RESIDUAL, s, [&] {
-    ob::launch_server(first ? ob::ServerPass::kResidualFirst : ob::ServerPass::kResidual, g, sa, s);
-  });
-  if (r) return r;
-  r = timed(c, ob::K_SCALE_FINALIZE, s, [&] {
-    ob::launch_scale_finalize(g, c->partials, g.num_tiles, 1, c->W, 1, g.piece_begin, g.piece_numel, c->S,
-                              scale_s, c->max_piece_tiles, s);
-  });
-  if (r) return r;
-  return do_update(c, false, ob::K_UPDATE_RESIDUAL, packed_s, scale_s, v, nullptr, params, lr, s);
+  return do_step_residual(c, first != 0, grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s,
+                          scale_s, lr, static_cast<hipStream_t>(stream), own_scratch(c), true);
 }
 
 int ob_materialize(ob_ctx *c, const float *x_w, const float *scale_w, const float *z,
@@ -531,7 +601,7 @@ int ob_begin_compression(ob_ctx *c, float *err_w, float *err_s, void *stream) {
 
 int ob_set_server_chunks(ob_ctx *c, int32_t chunks) {
   if (c == nullptr || chunks < 1) return OB_ERR_INVALID;
-  if (hipDeviceSynchronize() != hipSuccess) return OB_ERR_DEVICE;   // tables may be in use
+  if (wait_for_last_launch(c) != OB_OK) return OB_ERR_DEVICE;   // the tables may be in use
   return upload_pieces(c, chunks);
 }
 
@@ -549,7 +619,7 @@ int ob_cltk_configure(ob_ctx *c, double density, int64_t *k_total) {
     return OB_ERR_INVALID;
   for (int32_t t = 0; t < c->T; ++t)   // index entries are int32 positions within a tensor
     if (c->numel[t] > INT32_MAX) return OB_ERR_INVALID;
-  if (hipDeviceSynchronize() != hipSuccess) return OB_ERR_DEVICE;   // old tables may be in use
+  if (wait_for_last_launch(c) != OB_OK) return OB_ERR_DEVICE;   // the old tables may be in use
   std::vector<int64_t> k_off(static_cast<size_t>(c->T) + 1, 0);
   for (int32_t t = 0; t < c->T; ++t) {
     const int64_t k = std::max<int64_t>(1, static_cast<int64_t>(std::ceil(density * static_cast<double>(c->numel[t]))));

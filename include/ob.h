@@ -3,7 +3,8 @@
  * MI355X (gfx950).
  *
  * The method: the nubint.ai review of "1-bit Adam: Communication Efficient
- * Large-Scale Training with Adam's Convergence Speed" (Tang, Gan et al.).
+ * Large-Scale Training with Adam's Convergence Speed" (Tang, Gan et al.),
+ * called "the 1-bit Adam review" in the Source line of each declaration.
  * After a full-precision Adam warmup, Adam's variance is frozen and used as a
  * fixed preconditioner (Abstract; Proposed method, bullet 2), and training
  * continues as momentum SGD whose momentum is exchanged with 1-bit
@@ -94,7 +95,12 @@ const char *ob_status_string(int status);
  * pointer is NULL or some numel[t] is < 1 or > 2^40. */
 int ob_layout(int32_t num_tensors, const int64_t *numel, int64_t *elem_off);
 
-/* Creates a context for T tensors of numel[] elements (host array, copied),
+/* Source: the 1-bit Adam review, Proposed method, bullets 1 and 2: after the
+ * Adam warmup the optimizer is momentum SGD (momentum coefficient beta1)
+ * preconditioned by the frozen variance (eps in the denominator).  The flat
+ * tensor list and its layout are this library's.
+ *
+ * Creates a context for T tensors of numel[] elements (host array, copied),
  * 1 <= W <= 4096 simulated workers, gradients of grad_dtype, and the fixed
  * hyper-parameters beta1 (momentum, in [0, 1)) and eps (> 0 also once rounded
  * to fp32, the precision the kernels use it in).  Allocates the
@@ -114,7 +120,13 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
  * NULL is ignored. */
 void ob_destroy(ob_ctx *ctx);
 
-/* Workers [w_begin, w_end) ⊆ [0, W): momentum, error feedback, 1-bit
+/* Source: the 1-bit Adam review, Proposed method, bullet 3 (error-compensated
+ * compression applied to the momentum, not the gradient), Abstract (error
+ * compensation keeps convergence robust under 1-bit compression) and One-line
+ * summary (1-bit compression).  The scale ||x||_2/sqrt(n) and the bit layout
+ * are readings: the pages give no formula.
+ *
+ * Workers [w_begin, w_end) ⊆ [0, W): momentum, error feedback, 1-bit
  * compression and the new worker error.
  *   grads    [W][N] grad_dtype, read (rows w_begin..w_end-1)
  *   m        [N]    fp32, read (the shared momentum)
@@ -125,7 +137,13 @@ int ob_compress_worker(ob_ctx *ctx, int32_t w_begin, int32_t w_end, const void *
                        const float *m, float *err_w, uint64_t *packed_w, float *scale_w,
                        void *stream);
 
-/* Server: decompress and average all W messages, add the server error,
+/* Source: the 1-bit Adam review, Proposed method, bullet 4 (the compressed
+ * messages are exchanged through custom collectives).  The pages describe the
+ * collective only in prose; a server that averages the W decompressed messages
+ * and re-compresses the average with its own error buffer is the reading
+ * taken, and here the exchange is a local reduction in one GPU's memory.
+ *
+ * Server: decompress and average all W messages, add the server error,
  * re-compress, store the new server error.
  *   packed_w [W][Nw], scale_w [W][T] read; err_s [N] read and overwritten;
  *   packed_s [Nw] and scale_s [S] written (the server message; S = T unless the
@@ -133,13 +151,22 @@ int ob_compress_worker(ob_ctx *ctx, int32_t w_begin, int32_t w_end, const void *
 int ob_server_reduce(ob_ctx *ctx, const uint64_t *packed_w, const float *scale_w,
                      float *err_s, uint64_t *packed_s, float *scale_s, void *stream);
 
-/* Update from the server message with the frozen variance:
+/* Source: the 1-bit Adam review, Abstract (the variance, stable after warmup,
+ * is a fixed preconditioner for the rest of training), Proposed method, bullet
+ * 2, and One-line summary (preconditioned momentum SGD).  No bias correction,
+ * eps outside the root.
+ *
+ * Update from the server message with the frozen variance:
  *   packed_s [Nw], scale_s [S], v [N] read; m [N] written; params [N] read and
  *   overwritten.  lr must be finite. */
 int ob_apply_update(ob_ctx *ctx, const uint64_t *packed_s, const float *scale_s,
                     const float *v, float *m, float *params, double lr, void *stream);
 
-/* One whole compression-phase step: ob_compress_worker over all W workers,
+/* Source: the 1-bit Adam review, One-line summary and Proposed method, bullets
+ * 1 to 4: one step of the compression phase (compressed momentum, exchange,
+ * preconditioned update).
+ *
+ * One whole compression-phase step: ob_compress_worker over all W workers,
  * ob_server_reduce and ob_apply_update, with the server's second pass and the
  * update fused into one kernel.  Same buffers and results as the three calls
  * in sequence. */
@@ -147,7 +174,11 @@ int ob_step(ob_ctx *ctx, const void *grads, float *m, const float *v, float *par
             float *err_w, float *err_s, uint64_t *packed_w, float *scale_w,
             uint64_t *packed_s, float *scale_s, double lr, void *stream);
 
-/* The same step with the error and momentum state kept in residual form,
+/* Source: as ob_step (the 1-bit Adam review, One-line summary and Proposed
+ * method, bullets 1 to 4).  The residual form of the state between steps is
+ * this library's: the pages say nothing of what is stored between steps.
+ *
+ * The same step with the error and momentum state kept in residual form,
  * one pass per phase instead of two.
  *
  * Residual form: err_w[w] holds x_w, the value worker w compressed in the
@@ -171,7 +202,10 @@ int ob_step_residual(ob_ctx *ctx, int32_t first, const void *grads, const float 
                      uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s,
                      double lr, void *stream);
 
-/* Writes the strict-form state of a residual-form state:
+/* Source: the 1-bit Adam review, Proposed method, bullet 3: the error left by
+ * compressing x is x minus its 1-bit reconstruction.
+ *
+ * Writes the strict-form state of a residual-form state:
  *   err_w [W][N] = x_w - s_w,t*sign(x_w),  err_s [N] = z - s_s,t*sign(z),
  *   m [N] = s_s,t*sign(z).
  * x_w [W][N], scale_w [W][T], z [N], scale_s [S] are read.  Outputs may be
@@ -179,7 +213,10 @@ int ob_step_residual(ob_ctx *ctx, int32_t first, const void *grads, const float 
 int ob_materialize(ob_ctx *ctx, const float *x_w, const float *scale_w, const float *z,
                    const float *scale_s, float *err_w, float *err_s, float *m, void *stream);
 
-/* Warmup phase: one uncompressed Adam step on the workers' average gradient,
+/* Source: the 1-bit Adam review, Proposed method, bullet 1 (full-precision
+ * Adam for about the first 20% of steps).
+ *
+ * Warmup phase: one uncompressed Adam step on the workers' average gradient,
  * the first phase of the method (the review of "1-bit Adam ...", Proposed
  * method, bullet 1: full-precision Adam for about the first 20% of steps,
  * whose variance the compression phase then keeps fixed, bullet 2):
@@ -192,26 +229,41 @@ int ob_materialize(ob_ctx *ctx, const float *x_w, const float *scale_w, const fl
 int ob_warmup_step(ob_ctx *ctx, const void *grads, float *m, float *v, float *params,
                    double beta2, double lr, void *stream);
 
-/* The switch from warmup to compression: v is kept as it is from now on
+/* Source: the 1-bit Adam review, Proposed method, bullets 1 and 2 (the switch
+ * to compressed momentum SGD, with the variance kept fixed from then on).
+ *
+ * The switch from warmup to compression: v is kept as it is from now on
  * (frozen) and the error buffers start from zero.  Writes 0 to every tensor
  * element of err_w [W][N] and err_s [N] (padding untouched).  The next step
  * is ob_step, or ob_step_residual with first != 0. */
 int ob_begin_compression(ob_ctx *ctx, float *err_w, float *err_s, void *stream);
 
-/* Partitioned server: when the server role is split C ways, rank j holds
+/* Source: the 1-bit Adam review, Proposed method, bullet 4 (the custom
+ * collective).  One scale per server chunk is the reading for a server role
+ * split across ranks; the pages do not say.
+ *
+ * Partitioned server: when the server role is split C ways, rank j holds
  * chunk j of every tensor and compresses it with its own scale.  Chunk j of
  * an n-element tensor covers elements [j*S_t, min((j+1)*S_t, n)) with
  * S_t = 8192*ceil(ceil(n/8192)/C) (whole 8192-element blocks, so a chunk
  * boundary never splits a sign word); a tensor has ceil(n/S_t) <= C chunks.
  * After this call every server scale (scale_s, the server message) is per
  * chunk, in tensor order then chunk order; ob_server_scale_count gives their
- * number S.  C = 1 (the default) is one scale per tensor.  Synchronous (waits
- * for the device, then uploads small tables); changes of C between steps
- * also change what scale_s holds, so use it before the first step. */
+ * number S.  C = 1 (the default) is one scale per tensor; any C at or above
+ * a tensor's tile count gives that tensor one scale per 8192-element block.
+ * Synchronous: waits for the stream of this context's latest launch (which
+ * must still exist), then uploads small tables; if an upload fails it
+ * restores the previous setting's tables and returns OB_ERR_DEVICE.  Changes
+ * of C between steps also change what scale_s holds, so use it before the
+ * first step. */
 int ob_set_server_chunks(ob_ctx *ctx, int32_t chunks);
 int32_t ob_server_scale_count(const ob_ctx *ctx);
 
-/* Layer-wise trust ratio (the fugumt page on "1-bit LAMB": LAMB's layer-wise
+/* Source: the fugumt page on "1-bit LAMB: Communication Efficient Large-Scale
+ * Large-Batch Training with LAMB's Convergence Speed", Abstract (LAMB's layer-
+ * wise adaptive learning rates kept under 1-bit compression).
+ *
+ * Layer-wise trust ratio (the fugumt page on "1-bit LAMB": LAMB's layer-wise
  * adaptive learning rates kept under compressed communication; the page gives
  * no formula, this is the plainest reading).  With enable != 0 every update of
  * this context (ob_step, ob_step_residual, ob_apply_update) becomes, per
@@ -224,7 +276,12 @@ int32_t ob_server_scale_count(const ob_ctx *ctx);
  * more read of v and params.  weight_decay >= 0 and finite. */
 int ob_set_trust_ratio(ob_ctx *ctx, int32_t enable, double weight_decay);
 
-/* Cyclic local top-k (CLT-k), an alternative codec for the exchange: the
+/* Source: the nubint.ai review of "ScaleCom: Scalable Sparsified Gradient
+ * Compression for Communication-Efficient Distributed Training", Proposed
+ * method, bullet 1 (a cyclically chosen leader's top-k indices shared by all
+ * workers) and Main results, bullet 3.
+ *
+ * Cyclic local top-k (CLT-k), an alternative codec for the exchange: the
  * commutative compressor of the review of "ScaleCom: Scalable Sparsified
  * Gradient Compression for Communication-Efficient Distributed Training"
  * (Proposed method, bullet 1; Main results, bullet 3).  Per tensor t with
@@ -239,7 +296,8 @@ int ob_set_trust_ratio(ob_ctx *ctx, int32_t enable, double weight_decay);
  *
  * ob_cltk_configure allocates the codec's scratch for the given density
  * (0 < density <= 1; every n_t at most INT32_MAX, else OB_ERR_INVALID;
- * synchronous) and returns K = sum of k_t; ob_cltk_layout writes the host
+ * synchronous: waits for the stream of this context's latest launch, then
+ * allocates and uploads) and returns K = sum of k_t; ob_cltk_layout writes the host
  * array k_off[0..T] (tensor t's entries are k_off[t] .. k_off[t+1]-1).
  * ob_cltk_step: grads [W][N] read; memory [W][N] fp32 read and overwritten;
  * index [K] int32 (position within the tensor), values [W][K] fp32 and

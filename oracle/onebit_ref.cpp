@@ -136,6 +136,16 @@ float onebit_scale(const float *x, int64_t n) {
   return static_cast<float>(std::sqrt(q));
 }
 
+// gradient element i of a row-major array: fp32, or a bf16 bit pattern
+// widened exactly (bf16 is the upper half of the fp32 with the same value)
+float gradient(const void *g, int32_t bf16, size_t i) {
+  if (!bf16) return static_cast<const float *>(g)[i];
+  const uint32_t u = static_cast<uint32_t>(static_cast<const uint16_t *>(g)[i]) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
 bool sign_bit(float x) { return x >= 0.0f; }   // R2
 
 void pack_signs(const float *x, int64_t n, uint64_t *words) {
@@ -166,40 +176,48 @@ void ref_pack_signs(const float *x, int64_t n, uint64_t *words) { pack_signs(x, 
 // trust ratio of 1-bit LAMB (R14: u = m/(sqrt(v)+eps), plus wd*p when wd > 0;
 // r = fp32(sqrt(fl64(sum p^2)) / sqrt(fl64(sum u^2))), 1 when a sum is 0;
 // p - lr*(r*u)).
-//   g        [W][n] fp32 gradients (bf16 gradients widened by the caller: exact)
+//   g        [W] rows of n gradients, row w at g + w*ldg elements: fp32, or
+//            bf16 bit patterns (uint16) when g_bf16 != 0 (widened exactly: the
+//            bf16 bits are the upper half of the fp32 with the same value)
 //   p, m     [n] parameters and the shared momentum, read and overwritten
 //   v        [n] frozen variance
 //   err_s    [n] server error, read and overwritten
-//   err_w    [W][n] worker errors, read and overwritten
-//   packed_w [W][ceil(n/64)] and scale_w [W]: the worker messages (written)
+//   err_w    [W] rows of n worker errors (row w at err_w + w*lde), read and
+//            overwritten
+//   packed_w [W] rows of ceil(n/64) words (row w at packed_w + w*ldp) and
+//            scale_w[w*lds]: the worker messages (written)
 //   packed_s [ceil(n/64)] and scale_s [chunks]: the server message (written)
-// Returns 0, or 1 for a bad argument (n < 1, W < 1, C < 1, a null pointer).
-int ref_compression_step_opts(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
-                              int32_t chunks, int32_t trust, double wd, float *p, float *m, const float *v,
-                              float *err_s, float *err_w, uint64_t *packed_w, float *scale_w,
-                              uint64_t *packed_s, float *scale_s) {
+// The strides let a caller run the step in place on one tensor of a padded
+// flat list whose per-worker rows are N elements long.
+// Returns 0, or 1 for a bad argument (n < 1, W < 1, C < 1, a null pointer, a
+// stride shorter than a row).
+int ref_compression_step_strided(int64_t n, int32_t W, const void *g, int32_t g_bf16, int64_t ldg,
+                                 double beta1, double lr, double eps, int32_t chunks, int32_t trust, double wd,
+                                 float *p, float *m, const float *v, float *err_s, float *err_w, int64_t lde,
+                                 uint64_t *packed_w, int64_t ldp, float *scale_w, int64_t lds,
+                                 uint64_t *packed_s, float *scale_s) {
   if (n < 1 || W < 1 || chunks < 1 || !g || !p || !m || !v || !err_s || !err_w || !packed_w || !scale_w ||
       !packed_s || !scale_s)
     return 1;
-  const int64_t nw = (n + 63) / 64;
+  if (ldg < n || lde < n || ldp < (n + 63) / 64 || lds < 1) return 1;
   const float c1 = static_cast<float>(beta1);          // R5
   const float c2 = static_cast<float>(1.0 - beta1);
   std::vector<float> x(static_cast<size_t>(n));
 
   // workers, each on its own: momentum, error feedback, 1-bit message, new error
   for (int32_t w = 0; w < W; ++w) {
-    const float *gw = g + static_cast<size_t>(w) * n;
-    float *ew = err_w + static_cast<size_t>(w) * n;
-    uint64_t *words = packed_w + static_cast<size_t>(w) * nw;
+    float *ew = err_w + static_cast<size_t>(w) * lde;
+    uint64_t *words = packed_w + static_cast<size_t>(w) * ldp;
     for (int64_t i = 0; i < n; ++i) {
+      const float gi = gradient(g, g_bf16, static_cast<size_t>(w) * ldg + i);
       const float a = c1 * m[i];
-      const float b = c2 * gw[i];
+      const float b = c2 * gi;
       const float mw = a + b;
       x[i] = mw + ew[i];
     }
     const float s = onebit_scale(x.data(), n);
     pack_signs(x.data(), n, words);
-    scale_w[w] = s;
+    scale_w[static_cast<size_t>(w) * lds] = s;
     for (int64_t i = 0; i < n; ++i) ew[i] = x[i] - decompressed(words, s, i);   // e = x - C(x)
   }
 
@@ -208,7 +226,7 @@ int ref_compression_step_opts(int64_t n, int32_t W, const float *g, double beta1
   for (int64_t i = 0; i < n; ++i) {
     float acc = 0.0f;
     for (int32_t w = 0; w < W; ++w)
-      acc = acc + decompressed(packed_w + static_cast<size_t>(w) * nw, scale_w[w], i);
+      acc = acc + decompressed(packed_w + static_cast<size_t>(w) * ldp, scale_w[static_cast<size_t>(w) * lds], i);
     const float y = acc / wf;
     x[i] = y + err_s[i];
   }
@@ -250,6 +268,15 @@ int ref_compression_step_opts(int64_t n, int32_t W, const float *g, double beta1
     p[i] = p[i] - step;
   }
   return 0;
+}
+
+// The same step on contiguous [W][n] gradients (fp32), errors and messages.
+int ref_compression_step_opts(int64_t n, int32_t W, const float *g, double beta1, double lr, double eps,
+                              int32_t chunks, int32_t trust, double wd, float *p, float *m, const float *v,
+                              float *err_s, float *err_w, uint64_t *packed_w, float *scale_w,
+                              uint64_t *packed_s, float *scale_s) {
+  return ref_compression_step_strided(n, W, g, 0, n, beta1, lr, eps, chunks, trust, wd, p, m, v, err_s, err_w,
+                                      n, packed_w, (n + 63) / 64, scale_w, 1, packed_s, scale_s);
 }
 
 // The step with one server scale per tensor and the plain update.

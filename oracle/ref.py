@@ -70,6 +70,10 @@ def load() -> ctypes.CDLL:
                                               ctypes.c_double, ctypes.c_double, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_double, _f32p, _f32p, _f32p, _f32p, _f32p, _u64p, _f32p,
                                               _u64p, _f32p]
+    vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lib.ref_compression_step_strided.restype = ctypes.c_int
+    lib.ref_compression_step_strided.argtypes = [i64, i32, vp, i32, i64, dbl, dbl, dbl, i32, i32, dbl,
+                                                 vp, vp, vp, vp, vp, i64, vp, i64, vp, i64, vp, vp]
     lib.ref_warmup_step.restype = ctypes.c_int
     lib.ref_warmup_step.argtypes = [ctypes.c_int64, ctypes.c_int32, _f32p, ctypes.c_double, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f32p]
@@ -134,6 +138,57 @@ def compression_step(p, m, v, err_s, err_w, grads, beta1: float, lr: float, eps:
         raise ValueError("ref_compression_step_opts rejected its arguments")
     out["scale_s"] = out["scales_s"][0]
     return out
+
+
+def _addr(a: np.ndarray, dtype, index: int, count: int) -> int:
+    """Address of element `index` of the flat C-contiguous array `a`, after
+    checking that elements [index, index + count) lie inside it."""
+    if a.dtype != dtype or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"expected a C-contiguous {np.dtype(dtype)} array, got {a.dtype}")
+    if index < 0 or count < 0 or index + count > a.size:
+        raise IndexError(f"elements [{index}, {index + count}) outside an array of {a.size}")
+    return a.ctypes.data + index * a.itemsize
+
+
+def compression_step_in_place(lo: int, n: int, col: int, grads, p, m, v, err_s, err_w, packed_w, scale_w,
+                              packed_s, scale_s, beta1: float, lr: float, eps: float,
+                              server_chunks: int = 1, trust_wd=None) -> None:
+    """One step of the tensor at elements [lo, lo + n) of padded flat host
+    buffers, in place (lo a multiple of 64):
+      grads [W][N] fp32, or uint16 bf16 bit patterns;  p, m, v, err_s [N] fp32;
+      err_w [W][N] fp32;  packed_w [W][N/64] uint64;  scale_w [W][T] fp32 (column
+      col written);  packed_s [N/64] uint64;  scale_s this tensor's server
+      scales (a contiguous fp32 array of one entry per server chunk, written).
+    The same arithmetic as compression_step, without copying the tensor out."""
+    g = np.asarray(grads)
+    for a in (g, p, m, v, err_s, err_w, packed_w, scale_w, packed_s, scale_s):
+        if not a.flags["C_CONTIGUOUS"]:   # a flattening copy would take the writes
+            raise TypeError("every buffer must be C-contiguous")
+    W, N = g.shape
+    T = scale_w.shape[1]
+    if lo % 64 or n < 1 or lo + n > N or not 0 <= col < T:
+        raise ValueError("tensor range outside the flat layout")
+    if err_w.shape != (W, N) or packed_w.shape != (W, N // 64) or scale_w.shape[0] != W:
+        raise ValueError("per-worker buffers do not match the gradients' [W][N]")
+    blocks = -(-n // 8192)
+    pieces = -(-n // (8192 * -(-blocks // int(server_chunks))))
+    if scale_s.size != pieces:
+        raise ValueError(f"scale_s holds {scale_s.size} entries, the server has {pieces} chunks")
+    bf16 = g.dtype == np.uint16
+    gdt = np.uint16 if bf16 else np.float32
+    nw = (n + 63) // 64
+    last = (W - 1) * N + lo   # first element of the last row's range
+    st = load().ref_compression_step_strided(
+        n, W, _addr(g.reshape(-1), gdt, lo, last - lo + n), 1 if bf16 else 0, N,
+        float(beta1), float(lr), float(eps), int(server_chunks), 0 if trust_wd is None else 1,
+        0.0 if trust_wd is None else float(trust_wd),
+        _addr(p, np.float32, lo, n), _addr(m, np.float32, lo, n), _addr(v, np.float32, lo, n),
+        _addr(err_s, np.float32, lo, n), _addr(err_w.reshape(-1), np.float32, lo, last - lo + n), N,
+        _addr(packed_w.reshape(-1), np.uint64, lo // 64, (W - 1) * (N // 64) + nw), N // 64,
+        _addr(scale_w.reshape(-1), np.float32, col, (W - 1) * T + 1), T,
+        _addr(packed_s, np.uint64, lo // 64, nw), _addr(scale_s, np.float32, 0, pieces))
+    if st != 0:
+        raise ValueError("ref_compression_step_strided rejected its arguments")
 
 
 def warmup_step(p, m, v, grads, beta1: float, beta2: float, lr: float, eps: float) -> dict:

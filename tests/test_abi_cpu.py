@@ -109,3 +109,24 @@ def test_profile_kind_names(lib):
     names = [lib.ob_profile_kind_name(i).decode() for i in range(k)]
     assert names[0] == "worker_pass1" and "server_pass2_update" in names
     assert lib.ob_profile_kind_name(k) is None
+
+
+def test_every_method_declaration_cites_its_source():
+    """Each entry point that computes a step of the method carries, in the
+    comment above its declaration, the page and the section that define it."""
+    import re
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ob.h")
+    with open(path) as f:
+        text = f.read()
+    sections = ("Abstract", "Proposed method", "One-line summary", "Main results")
+    for name in ("ob_init", "ob_compress_worker", "ob_server_reduce", "ob_apply_update", "ob_step",
+                 "ob_step_residual", "ob_materialize", "ob_warmup_step", "ob_begin_compression",
+                 "ob_set_server_chunks", "ob_set_trust_ratio", "ob_cltk_configure"):
+        m = re.search(r"\n(?:int|int32_t|void) " + name + r"\(", text)
+        assert m, f"{name} is not declared"
+        end = text.rfind("*/", 0, m.start())
+        comment = text[text.rfind("/*", 0, end): end]
+        assert "Source:" in comment, f"{name}: no Source line in the comment above its declaration"
+        src = comment[comment.index("Source:"):]
+        assert ("review" in src or "page" in src) and any(s in src for s in sections), \
+            f"{name}: the Source line names no page and section"

@@ -56,3 +56,46 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr + r.stdout
+
+
+def test_summarize_reports_the_median_run_and_three_fractions():
+    wl = WORKLOADS["bert_large"]
+    n = sum(wl.numel)
+    steps = 20
+    runs = [0.140, 0.134, 0.150, 0.136, 0.138]          # seconds per run of 20 steps
+    per = {"worker_residual": 5.3, "server_residual": 0.59, "update_residual": 0.69, "scale_finalize": 0.02}
+    launches = {"worker_residual": 100, "server_residual": 100, "update_residual": 100, "scale_finalize": 200}
+    kernels = {k: (per[k] * launches[k], launches[k]) for k in per}
+    kernels.update({k: (0.0, 0) for k in bench.kernel_bytes_per_element(wl) if k not in kernels})
+    r = bench.summarize(wl, n, steps, runs, kernels, "no_counters_for_this_name")
+    assert r["repeats"] == 5
+    assert abs(r["ms_per_step"] - 138 / 20) < 1e-9                   # the median run
+    assert r["ms_per_step_min"] == round(134 / 20, 4) and r["ms_per_step_max"] == round(150 / 20, 4)
+    f = r["step_fraction"]
+    assert f["method_bytes_per_element"] == 126.0
+    assert abs(f["moved_bytes_per_element"] - (97.125 + 9.125 + 12.125)) < 1e-9   # the residual kernels' bytes
+    assert abs(f["by_bytes_moved"] / f["by_method_bytes"] - 118.375 / 126.0) < 1e-3
+    assert f["by_counters"] is None and r["roofline"]["kernel"] == "worker_residual"
+
+
+def test_cpu_baseline_runs_the_whole_list():
+    import torch
+    from synth import grads_for_step, init_state
+    from synth.workloads import Workload
+    wl = Workload(name="tiny", tensors=(("a", (1000,)), ("b", (8193,)), ("c", (64,))), workers=3,
+                  grad_dtype="f32", steps=1, g_sigma=1e-3, v_kind="sq_normal", v_a=1e-3, v_b=1e-12)
+    st = init_state(wl, "cpu")
+    g = grads_for_step(wl, 0, "cpu")
+    r = bench.cpu_baseline(wl, st, g, repeats=2)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    assert str(sum(wl.numel)) in r["sample"] and r["all_cores"]["repeats"] == 2
+    assert r["host_nproc"] >= 1 and r["cpu_model"]
+    assert torch.equal(st["p"], init_state(wl, "cpu")["p"])   # host copies: the caller's state is untouched
+
+
+def test_server_pieces_matches_the_partition():
+    for n in (1, 8192, 8193, 70001, 31254528):
+        for c in (1, 2, 3, 8, 1000):
+            blocks = -(-n // 8192)
+            size = 8192 * -(-blocks // c)
+            assert bench.server_pieces(n, c) == len(range(0, n, size))

@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import fullsize
 import oracle.ref as ref
 from harness import Run, log
 from synth import WORKLOADS, grads_for_step
@@ -48,70 +49,24 @@ def _same(a, b) -> bool:
     return a.shape == b.shape and np.array_equal(a, b)
 
 
-CASES = [("resnet50_w32", 3, 1, None), ("bert_large", 2, 1, None), ("bert_base_w64", 1, 1, None),
-         ("gpt_1p3b_bf16", 1, 1, None),
-         ("bert_large", 2, 8, None),     # the server partitioned 8 ways
-         ("bert_large", 2, 1, 0.01)]     # the trust-ratio update with weight decay
-CASE_IDS = ["resnet50_w32", "bert_large", "bert_base_w64", "gpt_1p3b_bf16", "bert_large_server8", "bert_large_trust"]
+# Every workload for its whole trajectory (the step counts of the workloads),
+# in both state forms; the partitioned server and the trust-ratio update on the
+# BERT-Large list for two steps.
+CONFIG_CASES = [("resnet50_w32", "residual"), ("bert_large", "residual"), ("bert_base_w64", "residual"),
+                ("gpt_1p3b_bf16", "residual"), ("resnet50_w32", "strict"), ("bert_large", "strict"),
+                ("bert_base_w64", "strict"), ("gpt_1p3b_bf16", "strict")]
 
 
-@pytest.mark.parametrize("name,steps,chunks,trust_wd", CASES, ids=CASE_IDS)
-def test_every_element_against_cpp_oracle(name, steps, chunks, trust_wd):
+@pytest.mark.parametrize("name,form", CONFIG_CASES, ids=[f"{n}-{f}" for n, f in CONFIG_CASES])
+def test_config_trajectory_every_element(name, form):
     wl = WORKLOADS[name]
-    threads = max(1, min(16, os.cpu_count() or 1))
-    log(f"{name}: {steps} residual-form steps (server chunks {chunks}, trust-ratio weight decay "
-        f"{trust_wd}), every tensor against the C++ oracle ({threads} threads)")
-    ref.load()
-    run = Run(wl, server_chunks=chunks, trust_wd=trust_wd)
-    off, W = run.off, wl.workers
-    host = {k: _host(run.state[k]) for k in ("p", "m", "v", "err_s", "err_w")}
-    # the oracle's own state, per tensor
-    states = []
-    for t, n in enumerate(wl.numel):
-        lo, hi = off[t], off[t] + n
-        states.append({k: np.ascontiguousarray(host[k][..., lo:hi]) for k in host})
-    del host
-    gbuf = None
-    words = floats = 0
-    for k in range(steps):
-        gbuf = grads_for_step(wl, k, "cuda", out=gbuf)
-        g = _host(gbuf)
-        run.step_residual(gbuf, first=(k == 0))
-        view = run.materialized()
-        torch.cuda.synchronize()
-        got = {"p": _host(run.state["p"]), "m": _host(view["m"]), "err_s": _host(view["err_s"]),
-               "err_w": _host(view["err_w"]), "packed_w": _host(run.bufs["packed_w"]),
-               "scale_w": _host(run.bufs["scale_w"]), "packed_s": _host(run.bufs["packed_s"]),
-               "scale_s": _host(run.bufs["scale_s"])}
-        del view
+    fullsize.trajectory(wl, form, wl.steps)
 
-        def check(t):
-            n = wl.numel[t]
-            lo, hi = off[t], off[t] + n
-            wlo, whi = lo // 64, lo // 64 + (n + 63) // 64
-            st = states[t]
-            c = ref.compression_step(st["p"], st["m"], st["v"], st["err_s"], st["err_w"],
-                                     np.ascontiguousarray(g[:, lo:hi]), wl.beta1, wl.lr, wl.eps,
-                                     server_chunks=chunks, trust_wd=trust_wd)
-            bad = [key for key, mine, dev in (
-                ("packed_w", c["packed_w"], got["packed_w"][:, wlo:whi]),
-                ("scale_w", c["scale_w"], got["scale_w"][:, t]),
-                ("packed_s", c["packed_s"], got["packed_s"][wlo:whi]),
-                ("scale_s", c["scales_s"], got["scale_s"][run.piece_base[t]:run.piece_base[t + 1]]),
-                ("p", c["p"], got["p"][lo:hi]), ("m", c["m"], got["m"][lo:hi]),
-                ("err_s", c["err_s"], got["err_s"][lo:hi]), ("err_w", c["err_w"], got["err_w"][:, lo:hi]),
-            ) if not _same(mine, dev)]
-            states[t] = {"p": c["p"], "m": c["m"], "v": st["v"], "err_s": c["err_s"], "err_w": c["err_w"]}
-            return t, bad, W * ((n + 63) // 64) + (n + 63) // 64, (3 + W) * n + W + c["scales_s"].size
 
-        with ThreadPoolExecutor(max_workers=threads) as pool:
-            results = list(pool.map(check, sorted(range(wl.num_tensors), key=lambda t: -wl.numel[t])))
-        failed = [(wl.tensors[t][0], bad) for t, bad, _, _ in results if bad]
-        words += sum(r[2] for r in results)
-        floats += sum(r[3] for r in results)
-        assert not failed, f"{name} step {k}: {len(failed)} tensors differ, first {failed[:3]}"
-        log(f"{name} step {k}: {words} sign words and {floats} floats compared, all bit-identical")
-        del got, g
+@pytest.mark.parametrize("chunks,trust_wd", [(8, None), (1, 0.01)], ids=["server8", "trust"])
+def test_bert_large_options_every_element(chunks, trust_wd):
+    """The server partitioned 8 ways, and the trust-ratio update with weight decay."""
+    fullsize.trajectory(WORKLOADS["bert_large"], "residual", 2, server_chunks=chunks, trust_wd=trust_wd)
 
 
 @pytest.mark.parametrize("name,steps", [("bert_large", 2), ("gpt_1p3b_bf16", 1)])

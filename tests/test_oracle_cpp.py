@@ -327,3 +327,73 @@ def test_partitioned_server_and_trust_ratio_equal_numpy_oracle(n, W, chunks, tru
             assert _same(c[key], getattr(out.state, key)), (k, key)
         st = out.state
         cst = {key: c[key] for key in ("p", "m", "err_s", "err_w")}
+
+
+@pytest.mark.parametrize("dtype,chunks,trust_wd", [("f32", 1, None), ("bf16", 1, None), ("f32", 2, None),
+                                                   ("f32", 1, 0.01)])
+def test_in_place_flat_step_equals_per_tensor_step(dtype, chunks, trust_wd):
+    """The in-place step over a padded flat list (row strides N, the layout the
+    device buffers use) equals the contiguous per-tensor step bit for bit, over
+    three chained steps; padding is neither read nor written."""
+    rng = _rng(29)
+    sizes, W = (1, 65, 8192, 8193, 20000, 70001), 3
+    off = [0]
+    for n in sizes:
+        off.append(off[-1] + (n + 63) // 64 * 64)
+    N, T = off[-1], len(sizes)
+    pieces = [-(-n // (8192 * -(-(-(-n // 8192)) // chunks))) for n in sizes]
+    pbase = np.concatenate([[0], np.cumsum(pieces)])
+    canary = np.float32(123.5)
+    flat = {k: np.full(N, canary, np.float32) for k in ("p", "m", "v", "err_s")}
+    flat["err_w"] = np.full((W, N), canary, np.float32)
+    per = []
+    for t, n in enumerate(sizes):
+        lo = off[t]
+        vals = {"p": rng.normal(0, 0.02, n), "m": rng.normal(0, 1e-3, n), "v": rng.normal(0, 1e-3, n) ** 2 + 1e-12,
+                "err_s": rng.normal(0, 1e-4, n)}
+        for k, x in vals.items():
+            flat[k][lo:lo + n] = x
+        flat["err_w"][:, lo:lo + n] = rng.normal(0, 1e-4, (W, n))
+        per.append({k: flat[k][..., lo:lo + n].copy() for k in flat})
+    packed_w = np.zeros((W, N // 64), np.uint64)
+    scale_w = np.zeros((W, T), np.float32)
+    packed_s = np.zeros(N // 64, np.uint64)
+    scale_s = np.zeros(pbase[-1], np.float32)
+    for step in range(3):
+        g32 = rng.normal(0, 1e-3, (W, N)).astype(np.float32)
+        g = (g32.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else g32
+        for t, n in enumerate(sizes):
+            lo, nw = off[t], (n + 63) // 64
+            ref.compression_step_in_place(lo, n, t, g, flat["p"], flat["m"], flat["v"], flat["err_s"], flat["err_w"],
+                                          packed_w, scale_w, packed_s, scale_s[pbase[t]:pbase[t + 1]], 0.9, 1e-4,
+                                          1e-8, server_chunks=chunks, trust_wd=trust_wd)
+            c = ref.compression_step(per[t]["p"], per[t]["m"], per[t]["v"], per[t]["err_s"], per[t]["err_w"],
+                                     np.ascontiguousarray(g[:, lo:lo + n]), 0.9, 1e-4, 1e-8, server_chunks=chunks,
+                                     trust_wd=trust_wd)
+            w0 = lo // 64
+            assert np.array_equal(packed_w[:, w0:w0 + nw], c["packed_w"]), (step, t)
+            assert np.array_equal(packed_s[w0:w0 + nw], c["packed_s"]), (step, t)
+            assert _same(scale_w[:, t], c["scale_w"]) and _same(scale_s[pbase[t]:pbase[t + 1]], c["scales_s"])
+            for k in ("p", "m", "err_s", "err_w"):
+                assert _same(flat[k][..., lo:lo + n], c[k]), (step, t, k)
+            per[t].update({k: c[k] for k in ("p", "m", "err_s", "err_w")})
+    for t, n in enumerate(sizes):   # padding untouched
+        pad = slice(off[t] + n, off[t + 1])
+        for k in flat:
+            assert np.all(flat[k][..., pad] == canary), (t, k)
+
+
+def test_in_place_flat_step_rejects_bad_ranges():
+    W, N = 2, 128
+    f = lambda *s: np.zeros(s, np.float32)   # noqa: E731
+    args = dict(grads=f(W, N), p=f(N), m=f(N), v=f(N), err_s=f(N), err_w=f(W, N),
+                packed_w=np.zeros((W, 2), np.uint64), scale_w=f(W, 1), packed_s=np.zeros(2, np.uint64),
+                scale_s=f(1), beta1=0.9, lr=1e-4, eps=1e-8)
+    with pytest.raises(ValueError):
+        ref.compression_step_in_place(64, 65, 0, **args)            # past the end
+    with pytest.raises(ValueError):
+        ref.compression_step_in_place(1, 10, 0, **args)             # not word-aligned
+    with pytest.raises(TypeError):
+        bad = dict(args, err_w=f(N, W).T)                            # not contiguous
+        ref.compression_step_in_place(0, 10, 0, **bad)
+    ref.compression_step_in_place(64, 64, 0, **args)                # the last whole tensor fits
