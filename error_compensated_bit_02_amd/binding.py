@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libob.so")
 
-OB_OK, OB_ERR_INVALID, OB_ERR_ALIGN, OB_ERR_NOMEM, OB_ERR_DEVICE = 0, 1, 2, 3, 4
+OB_OK, OB_ERR_INVALID, OB_ERR_ALIGN, OB_ERR_NOMEM, OB_ERR_DEVICE, OB_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
 OB_GRAD_F32, OB_GRAD_BF16 = 0, 1
 
 _c_void_p = ctypes.c_void_p
@@ -34,6 +34,7 @@ SIGNATURES = {
     "ob_apply_update": (ctypes.c_int, [_c_void_p] * 6 + [_f64, _c_void_p]),
     "ob_step": (ctypes.c_int, [_c_void_p] * 11 + [_f64, _c_void_p]),
     "ob_step_residual": (ctypes.c_int, [_c_void_p, _i32] + [_c_void_p] * 10 + [_f64, _c_void_p]),
+    "ob_step_residual_noalloc": (ctypes.c_int, [_c_void_p, _i32] + [_c_void_p] * 10 + [_f64, _c_void_p]),
     "ob_materialize": (ctypes.c_int, [_c_void_p] * 9),
     "ob_warmup_step": (ctypes.c_int, [_c_void_p] * 5 + [_f64, _f64, _c_void_p]),
     "ob_begin_compression": (ctypes.c_int, [_c_void_p] * 4),
@@ -239,11 +240,13 @@ class OneBitAdam:
         _check(st, "ob_step")
 
     def step_residual(self, first, grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s,
-                      scale_s, lr, stream=None) -> None:
-        """One step with err_w / err_s in residual form (see include/ob.h)."""
+                      scale_s, lr, stream=None, noalloc=False) -> None:
+        """One step with err_w / err_s in residual form (see include/ob.h);
+        noalloc=True calls ob_step_residual_noalloc (static scratch, no allocation)."""
         f32 = (torch.float32,)
         m_ptr = _ptr(m, f32, self.N, "m") if first else (None if m is None else _ptr(m, f32, self.N, "m"))
-        st = self.lib.ob_step_residual(
+        name = "ob_step_residual_noalloc" if noalloc else "ob_step_residual"
+        st = getattr(self.lib, name)(
             self._ctx, 1 if first else 0, self._grad_ptr(grads), m_ptr, _ptr(v, f32, self.N, "v"),
             _ptr(params, f32, self.N, "params"), _ptr(err_w, f32, self.W * self.N, "err_w"),
             _ptr(err_s, f32, self.N, "err_s"),
@@ -251,7 +254,7 @@ class OneBitAdam:
             _ptr(scale_w, f32, self.W * self.T, "scale_w"),
             _ptr(packed_s, (torch.int64,), self.Nw, "packed_s"),
             _ptr(scale_s, f32, self.S, "scale_s"), float(lr), _stream(stream))
-        _check(st, "ob_step_residual")
+        _check(st, name)
 
     def materialize(self, x_w, scale_w, z, scale_s, err_w, err_s, m, stream=None) -> None:
         """Strict-form errors and momentum from a residual-form state (may be in place)."""

@@ -51,6 +51,8 @@ struct ob_ctx {
   ob::Geometry geo{};
   double2 *partials = nullptr;     // (W+1) x num_tiles
   double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile (residual worker pass)
+  void *static_scratch = nullptr;  // the device's static no-allocation scratch (null if unresolved)
+  size_t static_need = 0;          // bytes of it the no-allocation step uses for this list
   bool profiling = false;
   bool launched = false;             // some kernel was enqueued, on last_stream the latest
   hipStream_t last_stream = nullptr;
@@ -70,6 +72,8 @@ static_assert(sizeof(kKindNames) / sizeof(kKindNames[0]) == ob::K_NUM_KINDS,
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Scratch sections start on 256-byte boundaries.
+size_t scratch_bytes(size_t b) { return (b + 255) / 256 * 256; }
 
 int check_ptr(const void *p) {
   if (p == nullptr) return OB_ERR_INVALID;
@@ -344,6 +348,8 @@ const char *ob_status_string(int status) {
     case OB_ERR_ALIGN: return "device pointer not aligned to 16 bytes";
     case OB_ERR_NOMEM: return "out of memory";
     case OB_ERR_DEVICE: return "HIP runtime or launch failure";
+    case OB_ERR_SCRATCH:
+      return "the tensor list needs more scratch than the 64 MiB static buffer of ob_step_residual_noalloc";
     default: return "unknown status";
   }
 }
@@ -472,6 +478,12 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->geo.W = c->W;
   c->geo.N = c->N;
   c->geo.Nw = c->N / 64;
+  // the no-allocation step's static scratch on this device, and what this list needs of it
+  c->static_need = b_part + b_cpart + b_ratio;
+  if (ob::static_scratch_address(&c->static_scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    c->static_scratch = nullptr;   // ob_step_residual_noalloc then reports OB_ERR_DEVICE
+  }
   const int pr = upload_pieces(c, 1);
   if (pr != OB_OK) {
     (void)hipFree(c->scratch);
@@ -567,6 +579,25 @@ int ob_step_residual(ob_ctx *c, int32_t first, const void *grads, const float *m
   if (first && (st = check_ptr(m)) != OB_OK) return st;
   return do_step_residual(c, first != 0, grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s,
                           scale_s, lr, static_cast<hipStream_t>(stream), own_scratch(c), true);
+}
+
+int ob_step_residual_noalloc(ob_ctx *c, int32_t first, const void *grads, const float *m, const float *v,
+                             float *params, float *err_w, float *err_s, uint64_t *packed_w, float *scale_w,
+                             uint64_t *packed_s, float *scale_s, double lr, void *stream) {
+  if (c == nullptr || !std::isfinite(lr)) return OB_ERR_INVALID;
+  int st = check_ptrs(grads, v, params, err_w, err_s, packed_w, scale_w, packed_s, scale_s);
+  if (st) return st;
+  if (first && (st = check_ptr(m)) != OB_OK) return st;
+  if (c->static_need > ob::kStaticScratchBytes) return OB_ERR_SCRATCH;
+  if (c->static_scratch == nullptr) return OB_ERR_DEVICE;   // the address lookup at ob_init failed
+  // the static buffer, laid out as the context's scratch: partials | chunk partials | ratios
+  unsigned char *base = static_cast<unsigned char *>(c->static_scratch);
+  const size_t b_part = scratch_bytes(ob::partials_count(c->W, c->num_tiles) * sizeof(double2));
+  const size_t b_cpart = scratch_bytes(ob::chunk_partials_count(c->W, c->num_tiles) * sizeof(double2));
+  const StepScratch x{reinterpret_cast<double2 *>(base), reinterpret_cast<double2 *>(base + b_part),
+                      reinterpret_cast<float *>(base + b_part + b_cpart)};
+  return do_step_residual(c, first != 0, grads, m, v, params, err_w, err_s, packed_w, scale_w, packed_s,
+                          scale_s, lr, static_cast<hipStream_t>(stream), x, false);
 }
 
 int ob_materialize(ob_ctx *c, const float *x_w, const float *scale_w, const float *z,

@@ -225,4 +225,12 @@ void launch_materialize(const Geometry &g, const MaterializeArgs &a, hipStream_t
 void launch_warmup(const Geometry &g, bool bf16, const WarmupArgs &a, hipStream_t s);
 void launch_zero_errors(const Geometry &g, float *err_w, float *err_s, hipStream_t s);
 
+// The no-allocation step's scratch: one static device array of this many
+// bytes per GPU (kernels.hip), which holds the step's partial sums and trust
+// ratios.  static_scratch_address resolves its device address on the current
+// device (once per device; later calls return the cached address) and
+// returns hipSuccess or the error of the lookup.
+constexpr size_t kStaticScratchBytes = size_t{64} << 20;
+hipError_t static_scratch_address(void **out);
+
 }  // namespace ob

@@ -39,6 +39,8 @@
 // sqrt and division are correctly rounded.
 #include "internal.h"
 
+#include <mutex>
+
 #pragma clang fp contract(off)
 
 namespace ob {
@@ -843,7 +845,32 @@ void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStr
     hipLaunchKernelGGL((worker_kernel<G, kPass2>), grid, block, 0, s, g, a);
 }
 
+// Scratch of the no-allocation step (ob_step_residual_noalloc): every GPU the
+// library runs on holds one copy until the process ends.  In host code its
+// name is only a handle for the symbol lookup below; kernels receive the
+// device address that lookup returns.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 }  // namespace
+
+hipError_t static_scratch_address(void **out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *address[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (address[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    address[dev] = p;
+  }
+  *out = address[dev];
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // launchers

@@ -79,7 +79,8 @@ typedef enum {
   OB_ERR_INVALID = 1,   /* null pointer, bad count, bad range, non-finite hyper-parameter */
   OB_ERR_ALIGN = 2,     /* a device pointer not aligned to 16 bytes */
   OB_ERR_NOMEM = 3,     /* device or host allocation failed */
-  OB_ERR_DEVICE = 4     /* a HIP runtime call or kernel launch failed */
+  OB_ERR_DEVICE = 4,    /* a HIP runtime call or kernel launch failed */
+  OB_ERR_SCRATCH = 5    /* the list needs more than ob_step_residual_noalloc's static scratch */
 } ob_status;
 
 typedef enum {
@@ -201,6 +202,29 @@ int ob_step_residual(ob_ctx *ctx, int32_t first, const void *grads, const float 
                      const float *v, float *params, float *err_w, float *err_s,
                      uint64_t *packed_w, float *scale_w, uint64_t *packed_s, float *scale_s,
                      double lr, void *stream);
+
+/* For callers that cannot allocate device memory when they step: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same step as ob_step_residual (same arguments, buffers and results),
+ * with every per-step scratch buffer -- the per-tile and per-chunk partial
+ * sums of squares and the trust ratios -- in one static device array of this
+ * library (64 MiB per GPU, held from the library's first use on that GPU
+ * until the process ends) instead of the context's scratch.  It allocates
+ * nothing: no hipMalloc, hipFree, event creation or allocating library call
+ * (so its launches are not timed by ob_profile_*); its device address is
+ * looked up once per GPU by ob_init.  A list needs (W+1)*tiles*16 +
+ * W*tiles*128 + T*4 bytes of it (tiles = its 8192-element tiles; each of the
+ * three sections rounded up to 256 bytes): 48 MB for the BERT-Large-shaped
+ * list at W = 8.  A list needing more than 64 MiB returns OB_ERR_SCRATCH
+ * before anything is enqueued; OB_ERR_DEVICE if ob_init could not look the
+ * array up.  Every context and call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams, two host threads) race on it.  Each
+ * call writes every scratch entry before reading it, so nothing is cleared
+ * between calls. */
+int ob_step_residual_noalloc(ob_ctx *ctx, int32_t first, const void *grads, const float *m,
+                             const float *v, float *params, float *err_w, float *err_s,
+                             uint64_t *packed_w, float *scale_w, uint64_t *packed_s,
+                             float *scale_s, double lr, void *stream);
 
 /* Source: the 1-bit Adam review, Proposed method, bullet 3: the error left by
  * compressing x is x minus its 1-bit reconstruction.
