@@ -16,17 +16,27 @@ namespace ob {
 // bit order.
 // Elements per tile (a multiple of 256); 8192 measured best on gfx950 for
 // the worker passes (4096 and 16384 were slower or spilled).
-#ifndef OB_TILE
-#define OB_TILE 8192
-#endif
-#ifndef OB_MAX_GROUP
-#define OB_MAX_GROUP 16
-#endif
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
-constexpr int kTile = OB_TILE;
+constexpr int kTile = 8192;
 constexpr int kSub = kTile / kWaves;
 constexpr int kPerLane = kSub / 64;
+
+// Lane `lane` of `old` replaced by the wavefront-uniform `value` (one
+// v_writelane_b32): the LLVM intrinsic, reached through its name.
+__device__ int amdgcn_writelane(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Sign word c of a wavefront goes to lane c, kept as two 32-bit halves.
+struct LaneWords {
+  uint32_t lo = 0, hi = 0;
+  __device__ __forceinline__ void put(uint64_t word, int c) {
+    lo = static_cast<uint32_t>(amdgcn_writelane(static_cast<int>(static_cast<uint32_t>(word)), c,
+                                                static_cast<int>(lo)));
+    hi = static_cast<uint32_t>(amdgcn_writelane(static_cast<int>(static_cast<uint32_t>(word >> 32)), c,
+                                                static_cast<int>(hi)));
+  }
+  __device__ __forceinline__ uint64_t get() const { return (static_cast<uint64_t>(hi) << 32) | lo; }
+};
 
 struct Tile {
   int64_t start;   // first element of the tile in the flat layout
@@ -114,7 +124,7 @@ struct WorkerArgs {
 // the workgroups resident at once stream few rows; fewer when the tile count
 // alone would leave the launch short of kMinBlocks workgroups (many small
 // launches of a small list would leave most of the 256 CUs idle at the tail).
-constexpr int kMaxGroup = OB_MAX_GROUP;
+constexpr int kMaxGroup = 16;
 constexpr int kMinBlocks = 8192;
 // A launch's work-items per dimension must fit in 32 bits: at most this many
 // workgroups of kBlock threads.

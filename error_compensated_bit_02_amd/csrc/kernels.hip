@@ -223,21 +223,21 @@ __device__ __forceinline__ void worker_tile(const Tile &tl, const Geometry &g, c
       continue;
     }
     double hi = 0.0, lo = 0.0;
-    uint64_t word = 0;
+    LaneWords word;
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
       const bool ok = in_tile<kFull>(tl, ln, c);
       const float mw = a.c1 * mr[c] + a.c2 * gv[c];
       const float x = ok ? mw + ev[c] : 0.0f;
       const uint64_t bal = __ballot(ok && x >= 0.0f);
-      if (ln.lane == c) word = bal;
+      word.put(bal, c);
       dd_accumulate(hi, lo, x);  // lanes outside the tile hold x = 0 and add nothing
     }
     // Non-temporal: the sign words are read only by the server pass.  Cached,
     // one 256-byte row piece per worker beside the other rows slowed a tiled
     // worker pass by ~7% at W = 64 (measured; no effect at W = 8).
     if (ln.lane < ln.nwords)
-      __builtin_nontemporal_store(word, &a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane]);
+      __builtin_nontemporal_store(word.get(), &a.packed_w[static_cast<size_t>(w) * g.Nw + (ln.base >> 6) + ln.lane]);
     const int slot = (w - w_lo) % kFlushRows;
     park_partial(sink, slot, ln.wave, hi, lo);
     if (slot == kFlushRows - 1 || w == w_hi - 1) flush_partials(sink, w - slot, slot + 1);
@@ -317,20 +317,20 @@ __device__ __forceinline__ void worker_chunk(const Tile &tl, int tile, int q, in
   }
   const float s = kMode == kResid ? a.scale_w[static_cast<size_t>(w) * g.T + t] : 0.0f;   // previous step's
   double hi = 0.0, lo = 0.0;
-  uint64_t word = 0;
+  LaneWords word;
 #pragma unroll
   for (int c = 0; c < kChunkPerLane; ++c) {
     const float e = (kMode == kResid) ? onebit_error(ev[c], s) : ev[c];
     const float mw = a.c1 * mr[c] + a.c2 * gv[c];
     const float x = ok(c) ? mw + e : 0.0f;
     const uint64_t bal = __ballot(ok(c) && x >= 0.0f);
-    if (lane == c) word = bal;
+    word.put(bal, c);
     dd_accumulate(hi, lo, x);   // lanes outside the tile hold x = 0 and add nothing
     if (ok(c)) ew[64 * c] = x;
   }
   // non-temporal: the sign words are read only by the server pass
   if (lane < nwords)
-    __builtin_nontemporal_store(word, &a.packed_w[static_cast<size_t>(w) * g.Nw + (base >> 6) + lane]);
+    __builtin_nontemporal_store(word.get(), &a.packed_w[static_cast<size_t>(w) * g.Nw + (base >> 6) + lane]);
   dd_wave_reduce(hi, lo);
   if (lane == 0) red[wave] = make_double2(hi, lo);
   __syncthreads();
@@ -527,18 +527,18 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, c
     flush_partials(sink, g.W, 1);
     return;
   }
-  uint64_t word = 0;
+  LaneWords word;
   if (kMode == kSResidFirst || kMode == kSResid) {
     double hi = 0.0, lo = 0.0;
 #pragma unroll
     for (int c = 0; c < kPerLane; ++c) {
       const bool ok = in_tile<kFull>(tl, ln, c);
       const uint64_t bal = __ballot(ok && z[c] >= 0.0f);
-      if (ln.lane == c) word = bal;
+      word.put(bal, c);
       dd_accumulate(hi, lo, z[c]);
       if (ok) es[64 * c] = z[c];
     }
-    if (ln.lane < ln.nwords) a.packed_s[(ln.base >> 6) + ln.lane] = word;
+    if (ln.lane < ln.nwords) a.packed_s[(ln.base >> 6) + ln.lane] = word.get();
     park_partial(sink, 0, ln.wave, hi, lo);
     flush_partials(sink, g.W, 1);
     return;
@@ -557,7 +557,7 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, c
     const bool ok = in_tile<kFull>(tl, ln, c);
     const bool bit = z[c] >= 0.0f;
     const uint64_t bal = __ballot(ok && bit);
-    if (ln.lane == c) word = bal;
+    word.put(bal, c);
     if (ok) {
       es[64 * c] = bit ? z[c] - ss : z[c] + ss;
       if (kMode == kS2Update) {
@@ -569,7 +569,7 @@ __device__ __forceinline__ void server_tile(const Tile &tl, const Geometry &g, c
       }
     }
   }
-  if (ln.lane < ln.nwords) a.packed_s[(ln.base >> 6) + ln.lane] = word;
+  if (ln.lane < ln.nwords) a.packed_s[(ln.base >> 6) + ln.lane] = word.get();
 }
 
 template <int kMode, bool kPow2>

@@ -156,17 +156,17 @@ __device__ __forceinline__ void window_tile(const TopkArgs &a, const Tile &tl, i
                                             const TileLanes &ln, const uint32_t (&key)[kPerLane],
                                             Window w, uint32_t *wcnt) {
   uint32_t nm = 0, ngt = 0;
-  uint64_t gtw = 0;   // lane c: word c of the above-window mask
+  LaneWords gtw;   // lane c: word c of the above-window mask
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) {
     const bool ok = slot_ok<kFull>(tl, ln, c);
     const uint32_t d0 = key[c] >> kShift0;
     const uint64_t bg = __ballot(ok && d0 > w.hi);
-    if (ln.lane == c) gtw = bg;
+    gtw.put(bg, c);
     nm += __popcll(__ballot(ok && d0 >= w.lo && d0 <= w.hi));
     ngt += __popcll(bg);
   }
-  if (ln.lane < ln.nwords) a.above[(ln.base >> 6) + ln.lane] = gtw;
+  if (ln.lane < ln.nwords) a.above[(ln.base >> 6) + ln.lane] = gtw.get();
   if (ln.lane == 0) {
     wcnt[ln.wave] = nm;
     wcnt[kWaves + ln.wave] = ngt;
