@@ -87,54 +87,79 @@ class FlatOracle:
         self.packed_s = np.zeros(N // 64, np.uint64)
         self.scale_s = np.zeros(run.piece_base[-1], np.float32)
 
-    def step_and_compare(self, g: np.ndarray, got: Dict[str, np.ndarray], pool: ThreadPoolExecutor):
-        """Runs the oracle's step on every tensor (largest first) and compares
-        each tensor with the device's outputs `got` as soon as it is done.
-        Returns [(tensor name, [differing buffers])] and the counts compared."""
+    def _pairs(self, t: int, got: Dict[str, np.ndarray]):
         wl, run, st = self.wl, self.run, self.state
-        off, pb, W = run.off, run.piece_base, wl.workers
+        off, pb = run.off, run.piece_base
+        n = wl.numel[t]
+        lo, hi = off[t], off[t] + n
+        wlo, whi = lo // 64, lo // 64 + (n + 63) // 64
+        return (("packed_w", self.packed_w[:, wlo:whi], got["packed_w"][:, wlo:whi]),
+                ("scale_w", self.scale_w[:, t], got["scale_w"][:, t]),
+                ("packed_s", self.packed_s[wlo:whi], got["packed_s"][wlo:whi]),
+                ("scale_s", self.scale_s[pb[t]:pb[t + 1]], got["scale_s"][pb[t]:pb[t + 1]]),
+                ("p", st["p"][lo:hi], got["p"][lo:hi]), ("m", st["m"][lo:hi], got["m"][lo:hi]),
+                ("err_s", st["err_s"][lo:hi], got["err_s"][lo:hi]),
+                ("err_w", st["err_w"][:, lo:hi], got["err_w"][:, lo:hi]))
+
+    def _counts(self, t: int):
+        n, W, pb = self.wl.numel[t], self.wl.workers, self.run.piece_base
+        return (W + 1) * ((n + 63) // 64), (3 + W) * n + W + (pb[t + 1] - pb[t])
+
+    def step(self, g: np.ndarray, got: Dict[str, np.ndarray], pool: ThreadPoolExecutor):
+        """Runs the oracle's step on every tensor (largest first), in place, and
+        compares each tensor with the device's outputs `got` as soon as it is
+        done.  Returns [(tensor name, [differing buffers])] and the counts
+        compared."""
+        wl, run, st = self.wl, self.run, self.state
+        off, pb = run.off, run.piece_base
 
         def one(t: int):
-            n = wl.numel[t]
-            lo, hi = off[t], off[t] + n
-            wlo, whi = lo // 64, lo // 64 + (n + 63) // 64
-            ref.compression_step_in_place(lo, n, t, g, st["p"], st["m"], st["v"], st["err_s"], st["err_w"],
-                                          self.packed_w, self.scale_w, self.packed_s,
+            ref.compression_step_in_place(off[t], wl.numel[t], t, g, st["p"], st["m"], st["v"], st["err_s"],
+                                          st["err_w"], self.packed_w, self.scale_w, self.packed_s,
                                           self.scale_s[pb[t]:pb[t + 1]], wl.beta1, wl.lr, wl.eps,
                                           server_chunks=run.server_chunks, trust_wd=self.trust_wd)
-            pairs = (("packed_w", self.packed_w[:, wlo:whi], got["packed_w"][:, wlo:whi]),
-                     ("scale_w", self.scale_w[:, t], got["scale_w"][:, t]),
-                     ("packed_s", self.packed_s[wlo:whi], got["packed_s"][wlo:whi]),
-                     ("scale_s", self.scale_s[pb[t]:pb[t + 1]], got["scale_s"][pb[t]:pb[t + 1]]),
-                     ("p", st["p"][lo:hi], got["p"][lo:hi]), ("m", st["m"][lo:hi], got["m"][lo:hi]),
-                     ("err_s", st["err_s"][lo:hi], got["err_s"][lo:hi]),
-                     ("err_w", st["err_w"][:, lo:hi], got["err_w"][:, lo:hi]))
-            bad = [key for key, mine, dev in pairs if not _same(mine, dev)]
-            words = (W + 1) * (whi - wlo)
-            floats = (3 + W) * n + W + (pb[t + 1] - pb[t])
-            return t, bad, words, floats
+            return (t, [key for key, mine, dev in self._pairs(t, got) if not _same(mine, dev)]) + self._counts(t)
 
-        order = sorted(range(wl.num_tensors), key=lambda t: -wl.numel[t])
-        results = list(pool.map(one, order))
-        failed = [(wl.tensors[t][0], bad) for t, bad, _, _ in results if bad]
+        return self._collect(pool.map(one, self._order()))
+
+    def compare(self, got: Dict[str, np.ndarray], pool: ThreadPoolExecutor):
+        """Compares the device's outputs `got` with the oracle's state as it is
+        (after step()), tensor by tensor."""
+        def one(t: int):
+            return (t, [key for key, mine, dev in self._pairs(t, got) if not _same(mine, dev)]) + self._counts(t)
+
+        return self._collect(pool.map(one, self._order()))
+
+    def _order(self):
+        return sorted(range(self.wl.num_tensors), key=lambda t: -self.wl.numel[t])
+
+    def _collect(self, results):
+        results = list(results)
+        failed = [(self.wl.tensors[t][0], bad) for t, bad, _, _ in results if bad]
         return failed, sum(r[2] for r in results), sum(r[3] for r in results)
 
 
-def trajectory(wl, form: str, steps: int, server_chunks: int = 1, trust_wd: Optional[float] = None) -> None:
-    """`steps` steps of `form` ("residual": ob_step_residual, its state
-    materialized after every step; "strict": ob_step) over the whole list,
-    every element compared with the C++ oracle after every step."""
+def trajectory(wl, forms, steps: int, server_chunks: int = 1, trust_wd: Optional[float] = None) -> None:
+    """`steps` steps of each state form in `forms` ("residual": ob_step_residual,
+    its state materialized after every step; "strict": ob_step), run side by
+    side from the same initial state on the same gradients, every element of
+    each compared after every step with one C++ oracle trajectory."""
     nthreads = threads()
-    log(f"{wl.name}: {steps} {form}-form steps (server chunks {server_chunks}, trust-ratio weight decay "
-        f"{trust_wd}), every element against the C++ oracle ({nthreads} threads)")
+    log(f"{wl.name}: {steps} steps of the {' and '.join(forms)} form(s) (server chunks {server_chunks}, "
+        f"trust-ratio weight decay {trust_wd}), every element against the C++ oracle ({nthreads} threads)")
     ref.load()
     t0 = time.time()
-    run = Run(wl, server_chunks=server_chunks, trust_wd=trust_wd)
-    oracle = FlatOracle(run, trust_wd)
+    runs = {}
+    for form in forms:
+        runs[form] = Run(wl, server_chunks=server_chunks, trust_wd=trust_wd)
+    oracle = FlatOracle(runs[forms[0]], trust_wd)
     gbuf = grads_for_step(wl, 0, "cuda")
-    outs = {"p": run.state["p"], "m": run.state["m"], "err_s": run.state["err_s"], "err_w": run.state["err_w"],
-            **{k: run.bufs[k] for k in ("packed_w", "scale_w", "packed_s", "scale_s")}}
-    mirror = Mirror({"grads": gbuf, **outs})
+
+    def outputs(run: Run) -> Dict[str, torch.Tensor]:
+        return {"p": run.state["p"], "m": run.state["m"], "err_s": run.state["err_s"],
+                "err_w": run.state["err_w"], **{k: run.bufs[k] for k in ("packed_w", "scale_w", "packed_s", "scale_s")}}
+
+    mirror = Mirror({"grads": gbuf, **outputs(runs[forms[0]])})
     log(f"  {wl.name}: set up in {time.time() - t0:.1f}s")
     words = floats = 0
     with ThreadPoolExecutor(max_workers=nthreads) as pool:
@@ -142,23 +167,30 @@ def trajectory(wl, form: str, steps: int, server_chunks: int = 1, trust_wd: Opti
             t0 = time.time()
             if k:
                 gbuf = grads_for_step(wl, k, "cuda", out=gbuf)
-            view = None
-            if form == "residual":
-                run.step_residual(gbuf, first=(k == 0))
-                view = run.materialized()
-                dev = {**outs, "m": view["m"], "err_s": view["err_s"], "err_w": view["err_w"]}
-            else:
-                run.step(gbuf)
-                dev = outs
-            mirror.pull({"grads": gbuf, **dev})
-            del view, dev
-            t1 = time.time()
-            failed, nw, nf = oracle.step_and_compare(mirror.view["grads"], mirror.view, pool)
-            words += nw
-            floats += nf
-            assert not failed, f"{wl.name} {form} step {k}: {len(failed)} tensors differ, first {failed[:3]}"
-            log(f"  {wl.name} {form} step {k}: {words} sign words and {floats} floats compared, all "
-                f"bit-identical (device + copies {t1 - t0:.1f}s, oracle + compare {time.time() - t1:.1f}s)")
-    run.ctx.close()
-    del run, oracle, mirror, outs, gbuf
+            mirror.pull({"grads": gbuf})
+            g = mirror.view["grads"]   # the forms' pulls below leave the gradients in place
+            for i, form in enumerate(forms):
+                run = runs[form]
+                view = None
+                if form == "residual":
+                    run.step_residual(gbuf, first=(k == 0))
+                    view = run.materialized()
+                    dev = {**outputs(run), "m": view["m"], "err_s": view["err_s"], "err_w": view["err_w"]}
+                else:
+                    run.step(gbuf)
+                    dev = outputs(run)
+                mirror.pull(dev)
+                del view, dev
+                if i == 0:
+                    failed, nw, nf = oracle.step(g, mirror.view, pool)
+                else:
+                    failed, nw, nf = oracle.compare(mirror.view, pool)
+                words += nw
+                floats += nf
+                assert not failed, f"{wl.name} {form} step {k}: {len(failed)} tensors differ, first {failed[:3]}"
+            log(f"  {wl.name} step {k}: {words} sign words and {floats} floats compared "
+                f"({' and '.join(forms)}), all bit-identical ({time.time() - t0:.1f}s)")
+    for run in runs.values():
+        run.ctx.close()
+    del runs, oracle, mirror, gbuf
     torch.cuda.empty_cache()
