@@ -318,6 +318,45 @@ def time_form(form, wl, ctx, grads, steps, warmup, stream, repeats):
     return runs, kernels, st
 
 
+def time_noalloc(wl, ctx, grads, steps, warmup, stream, repeats):
+    """The residual form through ob_step_residual_noalloc (the same kernels with
+    their scratch in the library's static buffer; it records no kernel events),
+    timed like time_form.  None when the list needs more than that buffer."""
+    import torch
+    from error_compensated_bit_02_amd.binding import OB_ERR_SCRATCH, OneBitError
+    from synth import init_state
+    st = init_state(wl, "cuda")
+    bufs = ctx.alloc("cuda")
+    sets = len(grads)
+
+    def step(k: int) -> None:
+        ctx.step_residual(k == 0, grads[k % sets], st["m"], st["v"], st["p"], st["err_w"], st["err_s"],
+                          bufs["packed_w"], bufs["scale_w"], bufs["packed_s"], bufs["scale_s"], wl.lr,
+                          stream=stream, noalloc=True)
+
+    try:
+        step(0)
+    except OneBitError as e:
+        if e.status == OB_ERR_SCRATCH:
+            return None
+        raise
+    for k in range(1, warmup):
+        step(k)
+    torch.cuda.synchronize()
+    runs, k0 = [], warmup
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step(k0 + k)
+        torch.cuda.synchronize()
+        runs.append(time.perf_counter() - t0)
+        k0 += steps
+    del st, bufs
+    med = sorted(runs)[len(runs) // 2]
+    return {"ms_per_step": round(med * 1e3 / steps, 4), "ms_per_step_min": round(min(runs) * 1e3 / steps, 4),
+            "ms_per_step_max": round(max(runs) * 1e3 / steps, 4), "repeats": repeats}
+
+
 def time_cltk(wl, ctx, grads, density, steps, warmup, stream):
     """Warmup, then `steps` timed exchanges of the cyclic local top-k codec
     (the leader cycles with the step).  Returns (seconds, kernels)."""
@@ -598,6 +637,13 @@ def main() -> int:
             f"{100 * r['step_fraction']['by_method_bytes']:.1f}% of peak by the method's bytes, "
             f"{100 * r['step_fraction']['by_bytes_moved']:.1f}% by the bytes moved")
 
+    noalloc = None
+    if "residual" in forms:
+        torch.cuda.empty_cache()
+        noalloc = time_noalloc(wl, ctx, grads, args.steps, max(1, args.warmup), stream, max(1, args.repeats))
+        if noalloc:
+            log(f"bench: residual through ob_step_residual_noalloc: {noalloc['ms_per_step']:.3f} ms/step")
+
     warm = None
     if not args.no_warmup_phase:
         torch.cuda.empty_cache()
@@ -638,6 +684,7 @@ def main() -> int:
     }
     if "strict" in results and forms[0] != "strict":
         result["strict_form"] = results["strict"]
+    result["residual_noalloc"] = noalloc
     result["warmup_phase"] = warm
     result["cltk"] = cltk
     torch.cuda.empty_cache()
