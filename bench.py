@@ -27,7 +27,9 @@ if ROOT not in sys.path:
 
 METRIC = "compressed optimizer-step elements/s and HBM GB/s (% of peak), 1 MI355X"
 CSRC = os.path.join(ROOT, "error_compensated_bit_02_amd", "csrc")
-SOURCES = ("kernels.hip", "topk.hip")   # the device code whose traffic the counters measured
+# The device code and the host code that picks its launch shapes: stored
+# counters count only while all of these are what they measured.
+SOURCES = ("kernels.hip", "topk.hip", "internal.h", "api.cpp")
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
 
 
@@ -78,8 +80,10 @@ def cltk_bytes_per_element(wl, density: float) -> dict:
     }
 
 
-def source_of(kernel: str) -> str:
-    return "topk.hip" if kernel.startswith("cltk_") else "kernels.hip"
+def sources_of(kernel: str) -> tuple:
+    """The files whose change makes a kernel's stored counters stale: its
+    device source, the shared layout constants and the launch code."""
+    return ("topk.hip" if kernel.startswith("cltk_") else "kernels.hip", "internal.h", "api.cpp")
 
 
 def sha256_of(name: str) -> str:
@@ -91,14 +95,15 @@ def sha256_of(name: str) -> str:
 def counter_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's
-    reading), or None when there is none or the kernel's source changed since."""
+    reading), or None when there is none or its sources or launch code changed
+    since."""
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    src = source_of(kernel)
-    if data.get("sources_sha256", {}).get(src) != sha256_of(src):
+    shas = data.get("sources_sha256", {})
+    if any(shas.get(src) != sha256_of(src) for src in sources_of(kernel)):
         return None
     per = data.get("per_launch_bytes", {}).get(kernel)
     return None if per is None else float(per)

@@ -599,7 +599,8 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // selection and gather.  Workgroups are (worker group, tile), group-major as
-// in the worker passes.  Each rebuilds its tile's selection from the mask of
+// in the worker passes; a group is one worker unless the list is long (see
+// gather_group_size).  Each rebuilds its tile's selection from the mask of
 // keys above the window and the candidates (read-only here, so groups need
 // no ordering): selected = key above the threshold, or at it with tie rank
 // < r; lane c of each wavefront keeps word c of the mask and the position of
