@@ -74,6 +74,50 @@ def test_cltk_ragged(W, density):
     log(f"cltk W={W} density={density}: {exact}/{total} values bit-identical")
 
 
+def test_cltk_grouped_gather_many_small_tensors():
+    """The gather gives each workgroup one worker only while the list has few
+    (worker, tile) pairs (at most 2^19); past that it streams groups of
+    workers.  31,500 tensors of 1 to 300 elements and three multi-tile ones
+    with W = 17 make 17 x 31.5k pairs: the grouped gather (groups of 9 and 8
+    workers) on ragged tiles, every element of every tensor against the
+    oracle, from the first exchange (no threshold prediction) on."""
+    from error_compensated_bit_02_amd import OneBitAdam
+    rng = np.random.default_rng(17)
+    sizes = [int(n) for n in rng.integers(1, 301, size=31500)] + [8193, 20000, 65573]
+    W, density, steps = 17, 0.01, 3
+    wl = _wl("cltk_many_small_w17", sizes, W, steps=steps)
+    tiles = sum((n + 8191) // 8192 for n in sizes)
+    assert W * tiles > 1 << 19
+    ctx = OneBitAdam(wl.numel, W, wl.grad_dtype, wl.beta1, wl.eps)
+    k_off = ctx.cltk_configure(density)
+    off, N = padded_layout(wl.numel)
+    mem = torch.zeros(W, N, device="cuda")
+    mem.normal_(0.0, 1e-3)
+    for t, n in enumerate(wl.numel):
+        mem[:, off[t] + n: off[t + 1]] = 0.0
+    ref_mem = mem.cpu().numpy()
+    index = torch.zeros(ctx.K, dtype=torch.int32, device="cuda")
+    values = torch.zeros(W, ctx.K, dtype=torch.float32, device="cuda")
+    average = torch.zeros(ctx.K, dtype=torch.float32, device="cuda")
+    for k in range(steps):
+        g = grads_for_step(wl, k, "cuda")
+        host_g = g.cpu().numpy()
+        ctx.cltk_step(k, g, mem, index, values, average)
+        torch.cuda.synchronize()
+        got_mem, got_idx = mem.cpu().numpy(), index.cpu().numpy()
+        got_vals, got_avg = values.cpu().numpy(), average.cpu().numpy()
+        for t, n in enumerate(wl.numel):
+            lo, hi, klo, khi = off[t], off[t] + n, k_off[t], k_off[t + 1]
+            out = ob.cltk_step(ref_mem[:, lo:hi], host_g[:, lo:hi], k, ob.cltk_k(n, density))
+            assert np.array_equal(got_idx[klo:khi], out.index), f"step {k} tensor {t}: index differs"
+            assert np.array_equal(got_vals[:, klo:khi].view(np.uint32), out.values.view(np.uint32)), (k, t)
+            assert np.array_equal(got_avg[klo:khi].view(np.uint32), out.average.view(np.uint32)), (k, t)
+            assert np.array_equal(got_mem[:, lo:hi].view(np.uint32), out.memory.view(np.uint32)), (k, t)
+            ref_mem[:, lo:hi] = out.memory
+        log(f"  {wl.name} cltk step {k}: {len(sizes)} tensors, every element bit-identical")
+    ctx.close()
+
+
 def test_cltk_ties_and_zeros():
     """Many equal magnitudes (ties broken by position) and zero memories."""
     wl = _wl("cltk_ties_w2", (5000, 64, 130), 2, steps=3)
