@@ -110,7 +110,7 @@ def counter_traffic(workload: str, kernel: str):
 
 
 # rocprofv3 kernel names -> the library's kernel kinds.  Every topk_ kernel
-# but the gather and the average belongs to the CLT-k select stage (ten
+# but the gather and the average belongs to the CLT-k select stage (eleven
 # launches); its bytes are summed per exchange (per topk_reset).
 
 
@@ -129,7 +129,7 @@ def kind_of(name: str):
         return "apply_update" if args[0] == "true" else "update_residual"
     if base.endswith("_kernel"):   # warmup, materialize, zero_errors, trust_norms, trust_ratio
         return base[: -len("_kernel")]
-    if base == "topk_gather":
+    if base in ("topk_gather", "topk_gather_chunk"):   # the tiled or the chunked shape
         return "cltk_gather"
     if base == "topk_average":
         return "cltk_average"

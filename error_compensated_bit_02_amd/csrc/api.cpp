@@ -727,7 +727,7 @@ int ob_cltk_step(ob_ctx *c, int64_t step, const void *grads, float *memory, int3
   a.values = values;
   a.average = average;
   a.leader = static_cast<int>(step % c->W);
-  a.wgroup = ob::gather_group_size(c->W, c->num_tiles);
+  a.wgroup = ob::worker_group_size(c->W, c->num_tiles);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int st2 = timed(c, ob::K_TOPK_SELECT, s,
                   [&] { ob::launch_topk(ob::TopkStage::kSelect, c->geo, c->bf16, a, s); });

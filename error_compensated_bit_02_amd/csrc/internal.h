@@ -120,7 +120,7 @@ struct WorkerArgs {
 };
 
 // Workers handled by one workgroup of a tiled worker pass (the strict form's
-// two passes, and the CLT-k gather of long lists).  At most kMaxGroup, so
+// two passes, and the tiled CLT-k gather of long lists).  At most kMaxGroup, so
 // the workgroups resident at once stream few rows; fewer when the tile count
 // alone would leave the launch short of kMinBlocks workgroups (many small
 // launches of a small list would leave most of the 256 CUs idle at the tail).
@@ -135,21 +135,6 @@ inline int worker_group_size(int workers, int num_tiles) {
   const int want = (kMinBlocks + num_tiles - 1) / num_tiles;
   if (groups < want) groups = want < workers ? want : workers;
   return (workers + groups - 1) / groups;
-}
-
-// Workers per workgroup of the CLT-k gather.  One (each workgroup streams one
-// worker's row of its tile; workgroups in worker-major order) on lists of at
-// most kGatherMaxTiles tiles with at most kGatherMaxPairs (worker, tile)
-// pairs; worker_group_size's grouping beyond either.  Measured on MI355X over
-// 8 to 105 GB per exchange: one worker per workgroup was 1.5-7% faster up to
-// 4.9e5 pairs, slower by ~2% from 6.4e5 pairs on (every workgroup re-reads
-// its tile's selection data, ~2 KB), and on a 160k-tile list slower or level
-// at every worker count.
-constexpr int64_t kGatherMaxPairs = int64_t{1} << 19;
-constexpr int kGatherMaxTiles = 1 << 16;
-inline int gather_group_size(int workers, int num_tiles) {
-  if (num_tiles <= kGatherMaxTiles && static_cast<int64_t>(workers) * num_tiles <= kGatherMaxPairs) return 1;
-  return worker_group_size(workers, num_tiles);
 }
 
 struct ServerArgs {
@@ -209,7 +194,7 @@ struct TopkArgs {
   uint32_t *cand;            // [N] per tile, its keys inside the first-digit window, compacted
   uint16_t *cand_pos;        // [N] their positions within the tile, ascending
   uint32_t *tile_m;          // [num_tiles] number of those keys
-  uint64_t *above;           // [Nw] bit per element: key above the window
+  uint64_t *above;           // [Nw] bit per element: key above the window; after the select stage, the selection
   uint32_t *pred;            // [T] first digit of the last threshold (the window's centre); kept
   uint32_t *miss;            // [T] 1 when this exchange's first digit fell outside the window
   uint32_t *tile_gt;         // [num_tiles] keys above the threshold
@@ -217,12 +202,13 @@ struct TopkArgs {
   int64_t *tile_eq_before;   // [num_tiles] keys at the threshold in earlier tiles of the tensor
   int64_t *tile_sel_off;     // [num_tiles] position of the tile's first selected entry
   int leader;                // worker whose values rank the positions
-  int wgroup;                // workers per workgroup in the gather pass (see gather_group_size)
+  int wgroup;                // workers per workgroup in the tiled gather (see worker_group_size)
 };
 
-// The codec's three stages: the leader's threshold (radix select, per-tile
-// counts and offsets), the selection with the index list and the gather of
-// every worker's message with the memory update, and the server's average.
+// The codec's three stages: the leader's threshold and the selection (radix
+// select, per-tile counts and offsets, the selection mask), the gather of the
+// index list and every worker's message with the memory update, and the
+// server's average.
 enum class TopkStage { kSelect, kGather, kAverage };
 void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &a, hipStream_t s);
 

@@ -493,10 +493,17 @@ __global__ __launch_bounds__(kBlock) void topk_pick(TopkArgs a, int shift) {
 // per-tile counts above and at the threshold, then per-tensor offsets
 // ---------------------------------------------------------------------------
 // Keys above the window were counted with the candidates; the candidates
-// give the rest.  Wavefronts take their tiles as in topk_hist_cand.
+// give the rest.  Wavefronts take their tiles as in topk_hist_cand.  The
+// candidates above the threshold join the keys above the window in the
+// tile's mask (a.above), gathered in the wavefront's own LDS words and ORed
+// into the mask at the end of the tile; the ties that are taken follow in
+// topk_ties, once the per-tensor scans have ranked them.
 __global__ __launch_bounds__(kBlock) void topk_tile_counts(Geometry g, TopkArgs a) {
+  __shared__ uint64_t bits_s[kWaves][kTile / 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint64_t *bits = bits_s[wave];
+  for (int i = lane; i < kTile / 64; i += 64) bits[i] = 0ull;
   const int tw0 = static_cast<int>(blockIdx.x) * kCandTiles + wave * kWaveTiles;
   const WaveTile mine = wave_tiles<kWaveTiles>(g, a, tw0, lane);
   const uint32_t tau_l = mine.m != 0u ? a.prefix[mine.tensor] : 0u;
@@ -505,19 +512,33 @@ __global__ __launch_bounds__(kBlock) void topk_tile_counts(Geometry g, TopkArgs 
     if (wt.m == 0u) continue;
     const uint32_t tau = __builtin_amdgcn_readlane(tau_l, j);
     const uint32_t *cand = a.cand + wt.start;
+    const uint16_t *cand_pos = a.cand_pos + wt.start;
     uint32_t gt = 0, eq = 0;
+    wave_sync();   // the words are clear
     for (uint32_t j0 = 0; j0 < wt.m; j0 += 64 * kCandUnroll) {   // uniform: ballots stay converged
       uint32_t key[kCandUnroll];
+      uint16_t pos[kCandUnroll];
 #pragma unroll
       for (int u = 0; u < kCandUnroll; ++u) {
         const uint32_t i = j0 + 64 * u + lane;
         key[u] = i < wt.m ? cand[i] : 0u;
+        pos[u] = i < wt.m ? cand_pos[i] : uint16_t{0};
       }
 #pragma unroll
       for (int u = 0; u < kCandUnroll; ++u) {
         const bool valid = j0 + 64 * u + lane < wt.m;
-        gt += __popcll(__ballot(valid && key[u] > tau));
+        const bool above = valid && key[u] > tau;
+        gt += __popcll(__ballot(above));
         eq += __popcll(__ballot(valid && key[u] == tau));
+        if (above) atomicOr(reinterpret_cast<unsigned long long *>(&bits[pos[u] >> 6]), 1ull << (pos[u] & 63));
+      }
+    }
+    wave_sync();   // every bit of the tile is in
+    for (int i = lane; i < kTile / 64; i += 64) {   // words past the tile's end stay 0
+      const uint64_t v = bits[i];
+      if (v) {
+        a.above[(wt.start >> 6) + i] |= v;
+        bits[i] = 0ull;
       }
     }
     if (lane == 0) {
@@ -597,22 +618,74 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
   }
 }
 
+// The ties that are taken: in a tile whose keys at the threshold start
+// before rank r of the tensor's ties (tile_eq_before < r), the first of them
+// in position order up to rank r join the mask.  Candidates are in ascending
+// position order, so a tie's rank is its count among the tile's earlier
+// candidates at the threshold.  Typically one tile per tensor holds any;
+// wavefronts take their tiles as in topk_tile_counts.
+__global__ __launch_bounds__(kBlock) void topk_ties(Geometry g, TopkArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tw0 = static_cast<int>(blockIdx.x) * kCandTiles + wave * kWaveTiles;
+  const WaveTile mine = wave_tiles<kWaveTiles>(g, a, tw0, lane);
+  int64_t take_l = 0;
+  uint32_t tau_l = 0u;
+  if (mine.m != 0u) {
+    const int tile = tw0 + lane;
+    take_l = taken_ties(a.krem[mine.tensor], a.tile_eq_before[tile], a.tile_eq[tile]);
+    tau_l = a.prefix[mine.tensor];
+  }
+  for (int j = 0; j < kWaveTiles; ++j) {
+    const WaveTile wt = wave_tile_at(mine, j);
+    const int64_t take = static_cast<int64_t>(readlane64(static_cast<uint64_t>(take_l), j));
+    if (wt.m == 0u || take == 0) continue;
+    const uint32_t tau = __builtin_amdgcn_readlane(tau_l, j);
+    const uint32_t *cand = a.cand + wt.start;
+    const uint16_t *cand_pos = a.cand_pos + wt.start;
+    int64_t run = 0;   // ties met so far in the tile
+    for (uint32_t j0 = 0; j0 < wt.m && run < take; j0 += 64) {   // uniform
+      const uint32_t i = j0 + lane;
+      const bool at_tau = i < wt.m && cand[i] == tau;
+      const uint64_t b = __ballot(at_tau);
+      if (at_tau && run + __popcll(b & lanemask_lt(lane)) < take) {
+        const uint32_t p = cand_pos[i];
+        atomicOr(reinterpret_cast<unsigned long long *>(&a.above[(wt.start >> 6) + (p >> 6)]), 1ull << (p & 63));
+      }
+      run += __popcll(b);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// selection and gather.  Workgroups are (worker group, tile), group-major as
-// in the worker passes; a group is one worker unless the list is long (see
-// gather_group_size).  Each rebuilds its tile's selection from the mask of
-// keys above the window and the candidates (read-only here, so groups need
-// no ordering): selected = key above the threshold, or at it with tie rank
-// < r; lane c of each wavefront keeps word c of the mask and the position of
-// its first selected entry.  The first group writes the index list; every
-// group then streams its workers.
+// gather.  After the select stage a.above holds each tile's selection: a bit
+// per element, set for the keys above the threshold and for the ties taken.
+// Every worker's row is streamed once: x = memory + g, the message at the
+// selected positions, the memory with them zeroed; worker 0 also writes the
+// index list.  Two shapes:
 //
-// A tile's selected entries are one contiguous run of positions in each
-// worker's message, so the workgroup stages all its workers' entries in LDS
-// and writes them with one coalesced pass at the end: written directly, each
-// would be a 4-byte store into a line that many other stores also write.
-// When the run times the workers exceeds kStage entries the entries are
-// written directly (at such densities the direct stores are nearly dense).
+// chunked (lists of at most kChunkedGatherTiles tiles): one workgroup per
+// (chunk of kChunk elements of a tile, worker), worker-major (chunks along
+// x, workers along y), lane l of wavefront v owning element kChunk/kWaves *
+// v + 64 c + l of the chunk, so lane c < kChunkPerLane holds the
+// wavefront's word c of the mask.  The row loads are issued first; the
+// chunk's first position is tile_sel_off plus the set bits of the tile's
+// earlier words, one word per thread, summed per wavefront and across them
+// in LDS behind the workgroup's one barrier.  Messages are written
+// directly.
+//
+// tiled (longer lists): workgroups are (worker group, tile), group-major as
+// in the strict worker passes; lane c of each wavefront holds word c of the
+// mask and the position of its first selected entry.  A tile's selected
+// entries are one contiguous run of positions in each worker's message, so
+// the workgroup stages all its workers' entries in LDS and writes them with
+// one coalesced pass at the end (when the run times the workers exceeds
+// kStage entries they are written directly; at such densities the direct
+// stores are nearly dense).
+//
+// Measured on MI355X side by side: the chunked shape is 6-8% faster at the
+// BERT-Large and BERT-base lists and level at ResNet-50; at the 160k-tile
+// GPT list it ran 20.6 ms per exchange where the tiled one ran 18.1-20.6.
 // ---------------------------------------------------------------------------
 constexpr int kStage = 4096;
 
@@ -638,49 +711,16 @@ __device__ __forceinline__ void flush_stage(const uint32_t *stage, uint32_t *out
   __syncthreads();   // the stage may be refilled
 }
 
-// The tile's selection: keys above the window (the mask), and the candidates
-// above the threshold or at it with tie rank < r.  The
-// candidates are in ascending position order, so a key at the threshold ranks
-// after tile_eq_before[tile] of them in earlier tiles and after those at the
-// threshold before it in the list.  Lane c of each wavefront then holds word c
-// of the mask and the position of its first selected entry.
-__device__ __forceinline__ TileSelection select_words(const Geometry &g, const TopkArgs &a,
-                                                      const Tile &tl, int tile, const TileLanes &ln,
-                                                      int64_t *wcnt, uint64_t *smask,
-                                                      uint32_t *stage, bool write_index) {
+// The tile's selection from the mask: lane c of each wavefront holds word c
+// of the wavefront's part and the position of its first selected entry.
+// With write_index, the tile's run of the index list (positions within the
+// tensor, ascending) is staged in LDS when it fits and written out.
+__device__ __forceinline__ TileSelection tile_selection(const Geometry &g, const TopkArgs &a,
+                                                        const Tile &tl, int tile, const TileLanes &ln,
+                                                        int64_t *wcnt, uint32_t *stage, bool write_index) {
   const int t = tl.tensor;
-  const uint32_t tau = a.prefix[t];
-  const int64_t r = a.krem[t];
-  const int tile_words = (tl.len + 63) / 64;
-  for (int i = threadIdx.x; i < tile_words; i += kBlock) smask[i] = a.above[(tl.start >> 6) + i];
-  __syncthreads();
-  const uint32_t m = a.tile_m[tile];   // uniform over the workgroup
-  const uint32_t *cand = a.cand + tl.start;
-  const uint16_t *cand_pos = a.cand_pos + tl.start;
-  int64_t eq_run = a.tile_eq_before[tile];
-  for (uint32_t j0 = 0; j0 < m; j0 += kBlock) {
-    const uint32_t j = j0 + threadIdx.x;
-    const bool valid = j < m;
-    const uint32_t key = valid ? cand[j] : 0u;
-    const bool at_tau = valid && key == tau;
-    const uint64_t be = __ballot(at_tau);
-    if (ln.lane == 0) wcnt[ln.wave] = __popcll(be);
-    __syncthreads();
-    int64_t before = 0, chunk = 0;
-    for (int v = 0; v < kWaves; ++v) {
-      if (v < ln.wave) before += wcnt[v];
-      chunk += wcnt[v];
-    }
-    const int64_t rank = eq_run + before + __popcll(be & lanemask_lt(ln.lane));
-    if (valid && (key > tau || (at_tau && rank < r))) {
-      const uint32_t p = cand_pos[j];
-      atomicOr(reinterpret_cast<unsigned long long *>(&smask[p >> 6]), 1ull << (p & 63));
-    }
-    eq_run += chunk;
-    __syncthreads();   // wcnt and the mask words are complete
-  }
   TileSelection sel;
-  sel.selw = ln.lane < ln.nwords ? smask[ln.wave * kPerLane + ln.lane] : 0ull;
+  sel.selw = ln.lane < ln.nwords ? a.above[(ln.base >> 6) + ln.lane] : 0ull;
   int64_t nsel = 0;
 #pragma unroll
   for (int c = 0; c < kPerLane; ++c) nsel += __popcll(readlane64(sel.selw, c));
@@ -693,7 +733,6 @@ __device__ __forceinline__ TileSelection select_words(const Geometry &g, const T
     if (v < ln.wave) pos += wcnt[v];
     sel.count += wcnt[v];
   }
-  // positions in ascending index order (index = position within the tensor)
   const int64_t tensor_start =
       tl.start - static_cast<int64_t>(tile - g.tile_begin[t]) * kTile;
   const int64_t k_end = a.k_off[t + 1];
@@ -720,11 +759,10 @@ __device__ __forceinline__ TileSelection select_words(const Geometry &g, const T
 
 template <typename G, bool kFull>
 __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a, const Tile &tl,
-                                            int tile, int w_lo, int w_hi, int64_t *wcnt,
-                                            uint64_t *smask, uint32_t *stage) {
+                                            int tile, int w_lo, int w_hi, int64_t *wcnt, uint32_t *stage) {
   const TileLanes ln = tile_lanes(tl);
   const int64_t k_end = a.k_off[tl.tensor + 1];
-  const TileSelection sel = select_words(g, a, tl, tile, ln, wcnt, smask, stage, w_lo == 0);
+  const TileSelection sel = tile_selection(g, a, tl, tile, ln, wcnt, stage, w_lo == 0);
   const int64_t staged_entries = sel.count * (w_hi - w_lo);
   const bool staged = staged_entries <= kStage;   // uniform over the workgroup
   for (int w = w_lo; w < w_hi; ++w) {
@@ -774,7 +812,6 @@ __device__ __forceinline__ void gather_tile(const Geometry &g, const TopkArgs &a
 template <typename G>
 __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   __shared__ int64_t wcnt[kWaves];
-  __shared__ uint64_t smask[kTile / 64];
   __shared__ uint32_t stage[kStage];
   const int tile = static_cast<int>(blockIdx.x % static_cast<unsigned>(g.num_tiles));
   const int grp = static_cast<int>(blockIdx.x / static_cast<unsigned>(g.num_tiles));
@@ -782,9 +819,90 @@ __global__ __launch_bounds__(kBlock) void topk_gather(Geometry g, TopkArgs a) {
   const int w_hi = min(g.W, w_lo + a.wgroup);
   const Tile tl = g.tiles[tile];
   if (tl.len == kTile)
-    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt, smask, stage);
+    gather_tile<G, true>(g, a, tl, tile, w_lo, w_hi, wcnt, stage);
   else
-    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt, smask, stage);
+    gather_tile<G, false>(g, a, tl, tile, w_lo, w_hi, wcnt, stage);
+}
+
+// The chunked shape.
+constexpr int kChunkedGatherTiles = 1 << 16;
+constexpr int kChunkSub = kChunk / kWaves;      // elements of a wavefront in a chunk
+constexpr int kChunkPerLane = kChunkSub / 64;   // mask words of a wavefront in a chunk
+
+template <typename G, bool kFull>
+__device__ __forceinline__ void gather_chunk(const Geometry &g, const TopkArgs &a, const Tile &tl, int tile,
+                                             int q, int w, int *sums) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub0 = q * kChunk + wave * kChunkSub;   // first element of this wavefront in the tile
+  const int64_t base = tl.start + sub0;
+  const int rem = tl.len - sub0;
+  const int nwords = kFull ? kChunkPerLane
+                           : (rem <= 0 ? 0 : (rem >= kChunkSub ? kChunkPerLane : (rem + 63) / 64));
+  auto ok = [&](int c) { return kFull || sub0 + 64 * c + lane < tl.len; };
+  const size_t row = static_cast<size_t>(w) * g.N + base + lane;
+  float *mem = a.memory + row;
+  const G *gw = static_cast<const G *>(a.grads) + row;
+  float x[kChunkPerLane];
+#pragma unroll
+  for (int c = 0; c < kChunkPerLane; ++c) {   // all loads first: the stores below may alias them
+    x[c] = 0.0f;
+    if (ok(c)) x[c] = mem[64 * c] + grad_at(gw + 64 * c);
+  }
+  const uint64_t selw = lane < nwords ? a.above[(base >> 6) + lane] : 0ull;
+  // the tile's words before this chunk (fewer than kBlock), one per thread
+  int before = static_cast<int>(threadIdx.x) < q * (kChunk / 64)
+                   ? __popcll(a.above[(tl.start >> 6) + threadIdx.x]) : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o);
+  int mine = 0;
+#pragma unroll
+  for (int c = 0; c < kChunkPerLane; ++c) mine += __popcll(readlane64(selw, c));
+  if (lane == 0) {
+    sums[wave] = mine;
+    sums[kWaves + wave] = before;
+  }
+  __syncthreads();
+  int64_t pos = a.tile_sel_off[tile];
+  for (int v = 0; v < kWaves; ++v) pos += sums[kWaves + v] + (v < wave ? sums[v] : 0);
+  // the memory in a loop of its own, one full-row store per slot
+#pragma unroll
+  for (int c = 0; c < kChunkPerLane; ++c) {
+    const bool sel = (readlane64(selw, c) >> lane) & 1ull;   // never set past the end
+    if (ok(c)) mem[64 * c] = sel ? 0.0f : x[c];
+  }
+  const int64_t k_end = a.k_off[tl.tensor + 1];   // pos stays below it when the selection holds k_t entries
+  const int64_t tensor_start = tl.start - static_cast<int64_t>(tile - g.tile_begin[tl.tensor]) * kTile;
+  float *vals = a.values + static_cast<size_t>(w) * a.K;
+#pragma unroll
+  for (int c = 0; c < kChunkPerLane; ++c) {
+    const uint64_t bs = readlane64(selw, c);
+    if ((bs >> lane) & 1ull) {
+      const int64_t at = pos + __popcll(bs & lanemask_lt(lane));
+      if (at < k_end) {
+        store_nt(vals + at, x[c]);
+        if (w == 0)
+          store_nt(reinterpret_cast<uint32_t *>(a.index) + at,
+                   static_cast<uint32_t>(base + 64 * c + lane - tensor_start));
+      }
+    }
+    pos += __popcll(bs);
+  }
+}
+
+template <typename G>
+__global__ __launch_bounds__(kBlock) void topk_gather_chunk(Geometry g, TopkArgs a) {
+  __shared__ int sums[2 * kWaves];   // per wavefront: its own entries, then the earlier words' entries
+  const int tile = static_cast<int>(blockIdx.x / kChunksPerTile);
+  const int q = static_cast<int>(blockIdx.x % kChunksPerTile);
+  const int w = static_cast<int>(blockIdx.y);
+  const Tile tl = g.tiles[tile];
+  const int rem = tl.len - q * kChunk;   // uniform over the workgroup
+  if (rem <= 0) return;                  // past the tile's end
+  if (rem >= kChunk)
+    gather_chunk<G, true>(g, a, tl, tile, q, w, sums);
+  else
+    gather_chunk<G, false>(g, a, tl, tile, q, w, sums);
 }
 
 // the server: average of the W messages, ascending workers from +0, then / W
@@ -833,6 +951,7 @@ void launch_select_typed(const Geometry &g, const TopkArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((topk_pick<9, false>), tensors, block, 0, s, a, kShift2);
   hipLaunchKernelGGL(topk_tile_counts, cand_grid, block, 0, s, g, a);
   hipLaunchKernelGGL(topk_offsets, tensors, block, 0, s, g, a);
+  hipLaunchKernelGGL(topk_ties, cand_grid, block, 0, s, g, a);
 }
 
 }  // namespace
@@ -847,6 +966,14 @@ void launch_topk(TopkStage stage, const Geometry &g, bool bf16, const TopkArgs &
         launch_select_typed<float>(g, a, s);
       break;
     case TopkStage::kGather: {
+      if (g.num_tiles <= kChunkedGatherTiles) {
+        const dim3 grid(static_cast<unsigned>(g.num_tiles) * kChunksPerTile, static_cast<unsigned>(g.W));
+        if (bf16)
+          hipLaunchKernelGGL(topk_gather_chunk<uint16_t>, grid, block, 0, s, g, a);
+        else
+          hipLaunchKernelGGL(topk_gather_chunk<float>, grid, block, 0, s, g, a);
+        break;
+      }
       const int groups = (g.W + a.wgroup - 1) / a.wgroup;
       const dim3 grid(static_cast<unsigned>(g.num_tiles) * groups);
       if (bf16)

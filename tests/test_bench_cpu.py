@@ -23,7 +23,9 @@ def test_kind_of_maps_every_library_kernel():
         "update_kernel<true, false>": "apply_update",
         "warmup_kernel<float, true>": "warmup",
         "topk_gather<float>": "cltk_gather",
+        "topk_gather_chunk<unsigned short>": "cltk_gather",
         "topk_average<true>": "cltk_average",
+        "topk_ties": "cltk_select",
         "topk_pass1<float>": "cltk_select",
         "topk_hist_shared<9, 11>": "cltk_select",
         "topk_reset": "cltk_select",
