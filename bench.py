@@ -120,8 +120,9 @@ def kind_of(name: str):
     if not m:
         return "copy" if "copyBuffer" in name else None
     base, args = m.group(1), [x.strip() for x in (m.group(2) or "").split(",")]
-    if base in ("worker_kernel", "worker_chunk_kernel"):   # strict (tiled) or residual (chunked)
-        return ("worker_pass1", "worker_pass2", "worker_residual_first", "worker_residual")[int(args[1])]
+    if base in ("worker_kernel", "worker_chunk_kernel"):   # tiled or chunked; mode 4 is pass 2 in chunks
+        return ("worker_pass1", "worker_pass2", "worker_residual_first", "worker_residual",
+                "worker_pass2")[int(args[1])]
     if base == "server_kernel":
         return ("server_pass1", "server_pass2", "server_pass2_update", "server_residual_first",
                 "server_residual")[int(args[0])]

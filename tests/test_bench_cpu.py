@@ -16,6 +16,7 @@ def test_kind_of_maps_every_library_kernel():
         "worker_chunk_kernel<float, 2>": "worker_residual_first",
         "worker_chunk_kernel<float, 3>": "worker_residual",
         "worker_chunk_kernel<unsigned short, 3>": "worker_residual",
+        "worker_chunk_kernel<float, 4>": "worker_pass2",
         "server_kernel<0, true>": "server_pass1",
         "server_kernel<2, false>": "server_pass2_update",
         "server_kernel<4, true>": "server_residual",
