@@ -618,12 +618,11 @@ __global__ __launch_bounds__(kBlock) void topk_offsets(Geometry g, TopkArgs a) {
   }
 }
 
-// The ties that are taken: in a tile whose keys at the threshold start
-// before rank r of the tensor's ties (tile_eq_before < r), the first of them
-// in position order up to rank r join the mask.  Candidates are in ascending
-// position order, so a tie's rank is its count among the tile's earlier
-// candidates at the threshold.  Typically one tile per tensor holds any;
-// wavefronts take their tiles as in topk_tile_counts.
+// The ties that are taken: a key at the threshold joins the mask when its
+// rank among the tensor's ties (tile_eq_before of its tile plus its count
+// among the tile's earlier candidates at the threshold: candidates are in
+// ascending position order) is below r.  Typically one tile per tensor holds
+// any; wavefronts take their tiles as in topk_tile_counts.
 __global__ __launch_bounds__(kBlock) void topk_ties(Geometry g, TopkArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -675,7 +674,7 @@ __global__ __launch_bounds__(kBlock) void topk_ties(Geometry g, TopkArgs a) {
 // directly.
 //
 // tiled (longer lists): workgroups are (worker group, tile), group-major as
-// in the strict worker passes; lane c of each wavefront holds word c of the
+// in the strict form's tiled worker passes; lane c of each wavefront holds word c of the
 // mask and the position of its first selected entry.  A tile's selected
 // entries are one contiguous run of positions in each worker's message, so
 // the workgroup stages all its workers' entries in LDS and writes them with
@@ -683,9 +682,10 @@ __global__ __launch_bounds__(kBlock) void topk_ties(Geometry g, TopkArgs a) {
 // kStage entries they are written directly; at such densities the direct
 // stores are nearly dense).
 //
-// Measured on MI355X side by side: the chunked shape is 6-8% faster at the
-// BERT-Large and BERT-base lists and level at ResNet-50; at the 160k-tile
-// GPT list it ran 20.6 ms per exchange where the tiled one ran 18.1-20.6.
+// Measured on MI355X side by side, bit-identical: the chunked shape takes the
+// gather 10-12% faster at the BERT-Large and BERT-base lists and 3% at
+// ResNet-50; at the 160k-tile GPT list it ran 20.5-20.7 ms where the tiled
+// one ran 18.1-20.6.
 // ---------------------------------------------------------------------------
 constexpr int kStage = 4096;
 
