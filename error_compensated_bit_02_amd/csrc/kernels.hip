@@ -38,6 +38,7 @@
 // and the file is compiled without contraction, so each rounds once; fp32
 // sqrt and division are correctly rounded.
 #include "internal.h"
+#include "worker_runs.h"
 
 #include <mutex>
 
@@ -899,17 +900,16 @@ void launch_worker_mode(int mode, const Geometry &g, const WorkerArgs &a, hipStr
   }
   if (mode == kResidFirst || (mode == kPass2 && sizeof(G) == 4)) {
     // worker-fastest, one launch per run of workers whose grid fits kMaxGrid
-    const int64_t per = kMaxGrid / chunks;   // >= 1
-    for (int w0 = a.w0; w0 < a.w1; w0 += static_cast<int>(per < a.w1 - w0 ? per : a.w1 - w0)) {
+    worker_runs(a.w0, a.w1, chunks, kMaxGrid, [&](int b0, int b1) {
       WorkerArgs b = a;
-      b.w0 = w0;
-      b.w1 = static_cast<int>(per < a.w1 - w0 ? w0 + per : a.w1);
-      const dim3 grid(static_cast<unsigned>(chunks * (b.w1 - b.w0)));
+      b.w0 = b0;
+      b.w1 = b1;
+      const dim3 grid(static_cast<unsigned>(chunks * (b1 - b0)));
       if (mode == kResidFirst)
         hipLaunchKernelGGL((worker_chunk_kernel<G, kResidFirst>), grid, block, 0, s, g, b);
       else
         hipLaunchKernelGGL((worker_chunk_kernel<G, kPass2Chunk>), grid, block, 0, s, g, b);
-    }
+    });
     return;
   }
   const int groups = (a.w1 - a.w0 + a.wgroup - 1) / a.wgroup;
