@@ -50,7 +50,7 @@ struct ob_ctx {
   void *scratch = nullptr;         // one device allocation: tiles | tile_begin | numel | partials
   ob::Geometry geo{};
   double2 *partials = nullptr;     // (W+1) x num_tiles
-  double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile (residual worker pass)
+  double2 *chunk_partials = nullptr;   // W x num_tiles * kChunksPerTile (chunked worker passes)
   void *static_scratch = nullptr;  // the device's static no-allocation scratch (null if unresolved)
   size_t static_need = 0;          // bytes of it the no-allocation step uses for this list
   bool profiling = false;
@@ -393,9 +393,10 @@ int ob_init(ob_ctx **out, int32_t num_tensors, const int64_t *numel, int32_t num
   c->N = off[num_tensors];
 
   // The largest launches must fit the device's grid limit: (worker group,
-  // tile) workgroups of the strict worker passes, (chunk, worker) workgroups
-  // of the residual one (chunks along x, workers along y), and the scale
-  // finalize's up to one workgroup per (worker, tensor).
+  // tile) workgroups of the tiled worker passes, the chunks of one worker
+  // (the chunked passes put workers along y, or split their worker-fastest
+  // grids into runs of workers that fit), and the scale finalize's up to one
+  // workgroup per (worker, tensor).
   int64_t nt = 0;
   for (int32_t t = 0; t < num_tensors; ++t) nt += (numel[t] + ob::kTile - 1) / ob::kTile;
   if (nt * ob::kChunksPerTile > ob::kMaxGrid) {

@@ -68,10 +68,12 @@ inline size_t partials_count(int W, int num_tiles) {
   return static_cast<size_t>(W + 1) * static_cast<size_t>(num_tiles);
 }
 
-// The residual worker pass works in chunks: one workgroup per (chunk of
-// kChunk elements of a tile, worker), lane l of wavefront v owning element
-// kChunk/kWaves * v + 64*c + l of the chunk, and one partial per chunk:
-// W rows of num_tiles * kChunksPerTile pairs (chunks past a tile's end hold 0).
+// The chunked worker passes (the residual form's, the first residual step's
+// and, with fp32 gradients, the strict pass 2) and the chunked CLT-k gather:
+// one workgroup per (chunk of kChunk elements of a tile, worker), lane l of
+// wavefront v owning element kChunk/kWaves * v + 64*c + l of the chunk.  The
+// passes with sums of squares keep one partial per chunk: W rows of
+// num_tiles * kChunksPerTile pairs (chunks past a tile's end hold 0).
 constexpr int kChunk = 1024;
 constexpr int kChunksPerTile = kTile / kChunk;
 static_assert(kTile % kChunk == 0 && kChunk % (64 * kWaves) == 0, "chunk shape");
@@ -115,7 +117,7 @@ struct WorkerArgs {
   double2 *partials;         // per-tile partials (strict passes)
   double2 *chunk_partials;   // per-chunk partials (residual passes)
   int w0, w1;                // workers [w0, w1)
-  int wgroup;                // workers per workgroup of the strict passes (see worker_group_size)
+  int wgroup;                // workers per workgroup of the tiled strict passes (see worker_group_size)
   float c1, c2;
 };
 

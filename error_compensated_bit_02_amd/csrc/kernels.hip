@@ -18,12 +18,13 @@
 // (bit l = element 64 c + l), so packing costs one compare per element.
 // Sums of squares are reduced per wavefront, parked in LDS, folded per tile
 // in a fixed order (two barriers per tile, none per worker) and per tensor by
-// scale_finalize.  Three passes take their tile in chunks of 1024 elements
+// scale_finalize.  Several passes take their tile in chunks of 1024 elements
 // instead, one workgroup per chunk (lane l of wavefront v owning element
-// 256 v + 64 c + l of the chunk): the parameter update, the warmup step and
-// the residual worker pass (one workgroup per (chunk, worker), one partial
-// sum per chunk).  On MI355X a stream runs faster in such 4 KB workgroups
-// taken in address order.
+// 256 v + 64 c + l of the chunk): the parameter update, the warmup step, the
+// residual worker pass and, with fp32 gradients, the strict form's pass 2
+// (one workgroup per (chunk, worker), one partial sum per chunk).  On MI355X
+// a read-modify-write stream runs faster in such 4 KB workgroups; the
+// read-mostly strict pass 1 keeps the tiles.
 //
 // Two forms of the state between steps:
 //   strict    err_w / err_s hold the errors and m the momentum (two passes
