@@ -102,3 +102,30 @@ def test_server_pieces_matches_the_partition():
             blocks = -(-n // 8192)
             size = 8192 * -(-blocks // c)
             assert bench.server_pieces(n, c) == len(range(0, n, size))
+
+
+def test_counter_traffic_is_dropped_when_its_sources_change(tmp_path, monkeypatch):
+    """Stored HBM counters count only for the sources they measured: a kernel's
+    own file plus the shared constants and the launch code."""
+    import json
+    shas = {s: bench.sha256_of(s) for s in bench.SOURCES}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "tiny_hbm_counters.json").write_text(json.dumps({
+        "sources_sha256": shas,
+        "per_launch_bytes": {"worker_residual": 1.0e9, "cltk_gather": 2.0e9}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.counter_traffic("tiny", "worker_residual") == 1.0e9
+    assert bench.counter_traffic("tiny", "cltk_gather") == 2.0e9
+    assert bench.counter_traffic("tiny", "server_residual") is None       # not measured
+    assert bench.counter_traffic("absent", "worker_residual") is None    # no file
+
+    def changed(name):
+        return lambda s: "0" * 64 if s == name else shas[s]
+    for name, stale in [("api.cpp", {"worker_residual", "cltk_gather"}),
+                        ("internal.h", {"worker_residual", "cltk_gather"}),
+                        ("kernels.hip", {"worker_residual"}),
+                        ("topk.hip", {"cltk_gather"})]:
+        monkeypatch.setattr(bench, "sha256_of", changed(name))
+        for kernel in ("worker_residual", "cltk_gather"):
+            got = bench.counter_traffic("tiny", kernel)
+            assert (got is None) == (kernel in stale), (name, kernel, got)
