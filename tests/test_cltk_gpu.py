@@ -163,6 +163,45 @@ def test_cltk_threshold_jumps():
     _run(wl, 0.05, wl.steps, grads_fn=grads_fn)
 
 
+def test_cltk_threshold_drops_below_the_window():
+    """A threshold far below the predicted window (memories cleared and the
+    gradients 10^4 times smaller) takes the fallback path for a downward
+    miss; the exchange after it is predicted again.  Every element of every
+    tensor against the oracle."""
+    from error_compensated_bit_02_amd import OneBitAdam
+    W, density = 3, 0.05
+    wl = _wl("cltk_drop_w3", RAGGED, W, steps=4)
+    scales = (1.0, 1.0, 1e-4, 1e-4)
+    ctx = OneBitAdam(wl.numel, W, wl.grad_dtype, wl.beta1, wl.eps)
+    k_off = ctx.cltk_configure(density)
+    off, N = padded_layout(wl.numel)
+    mem = torch.zeros(W, N, device="cuda")
+    ref_mem = mem.cpu().numpy()
+    index = torch.zeros(ctx.K, dtype=torch.int32, device="cuda")
+    values = torch.zeros(W, ctx.K, dtype=torch.float32, device="cuda")
+    average = torch.zeros(ctx.K, dtype=torch.float32, device="cuda")
+    for k, scale in enumerate(scales):
+        if k == 2:   # clear the memories: only the small gradients remain
+            mem.zero_()
+            ref_mem[:] = 0.0
+        g = grads_for_step(wl, k, "cuda") * scale
+        host_g = g.cpu().numpy()
+        ctx.cltk_step(k, g, mem, index, values, average)
+        torch.cuda.synchronize()
+        got_mem, got_idx = mem.cpu().numpy(), index.cpu().numpy()
+        got_vals, got_avg = values.cpu().numpy(), average.cpu().numpy()
+        for t, n in enumerate(wl.numel):
+            lo, hi, klo, khi = off[t], off[t] + n, k_off[t], k_off[t + 1]
+            out = ob.cltk_step(ref_mem[:, lo:hi], host_g[:, lo:hi], k, ob.cltk_k(n, density))
+            assert np.array_equal(got_idx[klo:khi], out.index), f"exchange {k} tensor {t}: index differs"
+            assert np.array_equal(got_vals[:, klo:khi].view(np.uint32), out.values.view(np.uint32)), (k, t)
+            assert np.array_equal(got_avg[klo:khi].view(np.uint32), out.average.view(np.uint32)), (k, t)
+            assert np.array_equal(got_mem[:, lo:hi].view(np.uint32), out.memory.view(np.uint32)), (k, t)
+            ref_mem[:, lo:hi] = out.memory
+        log(f"  {wl.name} exchange {k} (gradient scale {scale}): every element bit-identical")
+    ctx.close()
+
+
 def test_cltk_configure_rejects_bad_density():
     from error_compensated_bit_02_amd import OneBitAdam, OneBitError
     ctx = OneBitAdam((100, 7), 2, "f32", 0.9, 1e-8)
