@@ -36,13 +36,16 @@
 namespace ob {
 namespace {
 
+// A gradient element (bf16: the upper half of the same fp32, exact).  Each
+// pass reads a gradient row once: non-temporal loads (the gather 1-3%
+// faster on MI355X, bit-identical).
 template <typename G>
 __device__ __forceinline__ float grad_at(const G *p);
 template <>
-__device__ __forceinline__ float grad_at<float>(const float *p) { return *p; }
+__device__ __forceinline__ float grad_at<float>(const float *p) { return __builtin_nontemporal_load(p); }
 template <>
 __device__ __forceinline__ float grad_at<uint16_t>(const uint16_t *p) {
-  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  return __uint_as_float(static_cast<uint32_t>(__builtin_nontemporal_load(p)) << 16);
 }
 
 struct TileLanes {
